@@ -1,0 +1,248 @@
+"""Plain fp64 CPU oracle for the LightTransfer-Test hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
+code with the HIP library and never imports it; the product path does not
+import it either.
+
+Pieces:
+  * ``liblt_oracle.so`` (built from ``lt_oracle.c`` by :func:`build`): causal
+    attention with each softmax row materialised, its LSE, the per-row and
+    per-head lazy ratio, streaming attention and decode -- all in double.
+  * pure-Python host logic: the layer score, the lazy-layer priority queue,
+    the streaming-cache row set and the KV byte accounting.
+
+Sources (LightTransfer web pages; cited by page title and section):
+  * Chinese write-up (xzbcqc.com), "solution 2": a queue keyed by lazy ratio
+    is kept during prefill; once the number of queued layers exceeds the
+    threshold (e.g. 50% of layers) the highest-ratio layer is removed and its
+    KV cache switched to the streaming version.
+  * LightTransfer project page, Figure 2 caption: the queue stores (lazy
+    ratio, layer index) after each layer; the evicted layer's KV is reduced.
+  * Press-release page (wuwenjie.xyz), "LightTransfer method": the lazy ratio
+    sums the attention weights from queries to the initial and recent keys;
+    offline, the 50% of layers with the highest ratio are replaced.
+
+Readings where the pages are silent (each is listed in the design doc):
+  * the queue pushes first and pops while its size exceeds the capacity, so
+    the current layer can be evicted at its own step; equal scores evict the
+    lower layer index first;
+  * a layer's score is the mean of its per-head ratios over (batch, head);
+  * a streaming cache keeps rows [0, S) and [N-R, N), sinks first.
+
+Parity pins: tests/test_oracle_*.py (brute force in 50-digit arithmetic,
+torch fp64 library routines, closed forms, invariants, exhaustive queue
+checks).
+"""
+from __future__ import annotations
+
+import ctypes
+import heapq
+import math
+import os
+import subprocess
+from typing import Dict, List, Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lt_oracle.c")
+_LIB = os.path.join(_HERE, "liblt_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile lt_oracle.c into liblt_oracle.so with gcc and OpenMP."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Bind the oracle's C entry points from the shared library at ``path``."""
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.lto_prefill.argtypes = [ctypes.c_int] * 5 + [ctypes.c_double, dp, dp, dp] + \
+        [ctypes.c_int] * 3 + [dp] * 6
+    lib.lto_prefill.restype = ctypes.c_int
+    lib.lto_rows.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp,
+                             ctypes.c_int, ip, dp, ctypes.c_int, ctypes.c_int] + [dp] * 5
+    lib.lto_rows.restype = ctypes.c_int
+    lib.lto_decode.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, dp, dp, dp,
+                                                     ctypes.c_long, dp, dp]
+    lib.lto_decode.restype = ctypes.c_int
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a: Optional[np.ndarray]):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_double)()
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def default_scale(D: int) -> float:
+    """Softmax scale 1/sqrt(D) (the pages are silent; Flash Attention's default)."""
+    return 1.0 / math.sqrt(D)
+
+
+def prefill(q, k, v, S: int = 0, R: int = 1, W: int = 0, scale: Optional[float] = None,
+            streaming: bool = False, full: bool = True, lib=None) -> Dict[str, np.ndarray]:
+    """Causal GQA prefill; q [B,Hq,N,D], k/v [B,Hkv,N,D].
+
+    Returns out/lse (if ``full``), sout/slse (if ``streaming``) and, for W > 0,
+    lazy_rows [B,Hq,W] and lazy_ratio [B,Hq]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, N, D = q.shape
+    Hkv = k.shape[1]
+    assert k.shape == (B, Hkv, N, D) and v.shape == k.shape
+    sc = default_scale(D) if scale is None else float(scale)
+    res: Dict[str, np.ndarray] = {}
+    out = lse = sout = slse = lrows = lratio = None
+    if full:
+        out = np.empty((B, Hq, N, D)); lse = np.empty((B, Hq, N))
+        res["out"], res["lse"] = out, lse
+    if streaming:
+        sout = np.empty((B, Hq, N, D)); slse = np.empty((B, Hq, N))
+        res["sout"], res["slse"] = sout, slse
+    if W > 0:
+        lrows = np.empty((B, Hq, W)); lratio = np.empty((B, Hq))
+        res["lazy_rows"], res["lazy_ratio"] = lrows, lratio
+    rc = (lib or _load()).lto_prefill(B, N, Hq, Hkv, D, sc, _ptr(q), _ptr(k), _ptr(v), S, R, W,
+                             _ptr(out), _ptr(lse), _ptr(sout), _ptr(slse), _ptr(lrows),
+                             _ptr(lratio))
+    if rc != 0:
+        raise ValueError(f"lto_prefill failed with code {rc}")
+    return res
+
+
+def rows(k_head, v_head, positions: Sequence[int], q_rows, S: int = 0, R: int = 1,
+         scale: Optional[float] = None, lazy: bool = True,
+         streaming: bool = True, lib=None) -> Dict[str, np.ndarray]:
+    """Selected query rows of one head.  k_head/v_head [N,D] are the head's KV;
+    q_rows [n,D] are the queries at ``positions`` (each sees keys 0..pos)."""
+    k_head, v_head, q_rows = _f64(k_head), _f64(v_head), _f64(q_rows)
+    nk, D = k_head.shape
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int32))
+    n = pos.shape[0]
+    assert q_rows.shape == (n, D)
+    sc = default_scale(D) if scale is None else float(scale)
+    out = np.empty((n, D)); lse = np.empty(n)
+    lz = np.empty(n) if lazy else None
+    so = np.empty((n, D)) if streaming else None
+    sl = np.empty(n) if streaming else None
+    rc = (lib or _load()).lto_rows(nk, D, sc, _ptr(k_head), _ptr(v_head), n,
+                          pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), _ptr(q_rows),
+                          S, R, _ptr(out), _ptr(lse), _ptr(lz), _ptr(so), _ptr(sl))
+    if rc != 0:
+        raise ValueError(f"lto_rows failed with code {rc}")
+    res = {"out": out, "lse": lse}
+    if lazy:
+        res["lazy"] = lz
+    if streaming:
+        res["sout"], res["slse"] = so, sl
+    return res
+
+
+def decode(q, k_cache, v_cache, scale: Optional[float] = None, lib=None) -> Dict[str, np.ndarray]:
+    """One decode query per (b, h): q [B,Hq,D]; caches [B,Hkv,L,D] (all L rows seen)."""
+    q, k_cache, v_cache = _f64(q), _f64(k_cache), _f64(v_cache)
+    B, Hq, D = q.shape
+    _, Hkv, L, _ = k_cache.shape
+    sc = default_scale(D) if scale is None else float(scale)
+    out = np.empty((B, Hq, D)); lse = np.empty((B, Hq))
+    rc = (lib or _load()).lto_decode(B, Hq, Hkv, D, sc, _ptr(q), _ptr(k_cache), _ptr(v_cache), L,
+                            _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError(f"lto_decode failed with code {rc}")
+    return {"out": out, "lse": lse}
+
+
+# ---------------------------------------------------------------------------
+# Host-side selection (pure Python; small inputs by nature: one entry per layer)
+# ---------------------------------------------------------------------------
+
+def layer_score(head_ratio_row: Sequence[float]) -> float:
+    """A layer's score: the mean of its per-(batch, head) lazy ratios, summed in
+    fp64 in row-major order (the pages decide per layer and never mention heads)."""
+    acc = 0.0
+    for x in head_ratio_row:
+        acc += float(x)
+    return acc / len(head_ratio_row)
+
+
+def select_lazy_layers(scores: Sequence[float], capacity: int) -> Tuple[List[int], List[int]]:
+    """Priority queue keyed by lazy ratio, updated after each layer.
+
+    Layer l is pushed as (score, l); while the queue holds more than
+    ``capacity`` layers, the highest score leaves (equal scores: lower layer
+    index first) and becomes a streaming layer.  Returns
+    (evicted_at_step [L] with -1 for none, is_streaming [L] as 0/1)."""
+    L = len(scores)
+    if not (0 <= capacity <= L):
+        raise ValueError("capacity must lie in [0, L]")
+    heap: List[Tuple[float, int]] = []
+    evicted = [-1] * L
+    streaming = [0] * L
+    for l, s in enumerate(scores):
+        s = float(s)
+        if math.isnan(s) or math.isinf(s):
+            raise ValueError("scores must be finite")
+        heapq.heappush(heap, (-s, l))
+        if len(heap) > capacity:
+            _, victim = heapq.heappop(heap)
+            evicted[l] = victim
+            streaming[victim] = 1
+    return evicted, streaming
+
+
+def streaming_rows(N: int, S: int, R: int) -> List[int]:
+    """Rows a streaming KV cache keeps: the sinks [0, S) then the recent
+    [N-R, N); every row when N <= S + R.  This is the sink + recent set of the
+    last query, N-1."""
+    if N <= S + R:
+        return list(range(N))
+    return list(range(S)) + list(range(N - R, N))
+
+
+def kv_bytes(B: int, Hkv: int, N: int, D: int, elem: int, S: int, R: int) -> Tuple[int, int]:
+    """(full, streaming) KV bytes of one layer: K and V, B*Hkv heads, D each."""
+    full = 2 * B * Hkv * N * D * elem
+    stream = 2 * B * Hkv * min(N, S + R) * D * elem
+    return full, stream
+
+
+def kv_accounting(evicted_at_step: Sequence[int], full: int, stream: int) -> Dict[str, List[int]]:
+    """Per-step KV bytes while prefill walks the layers.
+
+    transient[l]: every layer so far at its current size plus layer l at full
+    size, before the queue's pop.  retained[l]: the same after the pop."""
+    L = len(evicted_at_step)
+    is_stream = [False] * L
+    retained, transient = [], []
+    for l in range(L):
+        before = sum(stream if is_stream[x] else full for x in range(l)) + full
+        ev = evicted_at_step[l]
+        if ev >= 0:
+            is_stream[ev] = True
+        after = sum(stream if is_stream[x] else full for x in range(l + 1))
+        transient.append(before)
+        retained.append(after)
+    return {"transient": transient, "retained": retained}

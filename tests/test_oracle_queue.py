@@ -1,0 +1,102 @@
+"""Pin the oracle's lazy-layer queue and KV accounting.
+
+Chinese write-up, "solution 2" / project page, Figure 2 caption: after each
+layer its (lazy ratio, layer) enters a priority queue; while more than C
+layers are queued the highest ratio leaves and its KV becomes streaming.
+Pins: a brute-force scan simulation (no heap), the closed form "the final
+full layers are the C lowest scores" (which is also the offline rule of the
+press-release page, "LightTransfer method": replace the 50% of layers with
+the highest ratio), exhaustive small cases with ties, capacity edges, and the
+byte totals of the 64-layer 32K workload.
+"""
+import itertools
+import random
+
+import pytest
+
+import oracle
+
+
+def scan_simulation(scores, C):
+    """Push, then remove the max by a linear scan while size > C (equal
+    scores: lower layer index leaves first)."""
+    held, ev = [], []
+    for l, s in enumerate(scores):
+        held.append((s, l))
+        e = -1
+        if len(held) > C:
+            best = max(held, key=lambda t: (t[0], -t[1]))
+            held.remove(best)
+            e = best[1]
+        ev.append(e)
+    return ev
+
+
+def closed_form_kept(scores, C):
+    order = sorted(range(len(scores)), key=lambda l: (scores[l], -l))
+    return set(order[:C])
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_queue_random(seed):
+    rnd = random.Random(seed)
+    L = rnd.randint(1, 40)
+    C = rnd.randint(0, L)
+    scores = [rnd.choice([rnd.random(), round(rnd.random(), 1)]) for _ in range(L)]
+    ev, st = oracle.select_lazy_layers(scores, C)
+    assert ev == scan_simulation(scores, C)
+    kept = {l for l in range(L) if not st[l]}
+    assert kept == closed_form_kept(scores, C)
+    assert sum(st) == L - C
+    assert sorted(e for e in ev if e >= 0) == sorted(l for l in range(L) if st[l])
+
+
+def test_queue_exhaustive_with_ties():
+    vals = (0.0, 0.5, 1.0)
+    for L in range(1, 7):
+        for scores in itertools.product(vals, repeat=L):
+            for C in range(0, L + 1):
+                ev, st = oracle.select_lazy_layers(list(scores), C)
+                assert ev == scan_simulation(list(scores), C)
+                assert {l for l in range(L) if not st[l]} == closed_form_kept(list(scores), C)
+
+
+def test_queue_capacity_edges():
+    s = [0.3, 0.9, 0.1, 0.5]
+    ev, st = oracle.select_lazy_layers(s, 4)
+    assert ev == [-1] * 4 and st == [0] * 4
+    ev, st = oracle.select_lazy_layers(s, 0)
+    assert ev == [0, 1, 2, 3] and st == [1] * 4
+    with pytest.raises(ValueError):
+        oracle.select_lazy_layers(s, 5)
+    with pytest.raises(ValueError):
+        oracle.select_lazy_layers([0.1, float("nan")], 1)
+
+
+def test_tie_breaks_lower_index_first():
+    ev, st = oracle.select_lazy_layers([0.5, 0.5, 0.5], 1)
+    assert ev == [-1, 0, 1] and st == [1, 1, 0]
+
+
+def test_layer_score_is_mean():
+    assert oracle.layer_score([0.25, 0.75, 0.5]) == 0.5
+
+
+def test_kv_accounting_driver_workload():
+    """64 layers of B1 Hkv8 N32768 D128 bf16, S4 R1020, capacity 32: all-full
+    8192 MiB, final 4224 MiB (32 full + 32 streaming), transient peak
+    4348 MiB (33 full + 31 streaming, at the last layer)."""
+    MiB = 1 << 20
+    full, stream = oracle.kv_bytes(1, 8, 32768, 128, 2, 4, 1020)
+    assert full == 128 * MiB and stream == 4 * MiB
+    scores = [random.Random(1).random() for _ in range(64)]
+    ev, st = oracle.select_lazy_layers(scores, 32)
+    acc = oracle.kv_accounting(ev, full, stream)
+    assert acc["retained"][-1] == 4224 * MiB
+    assert max(acc["transient"]) == 4348 * MiB
+    assert acc["transient"][-1] == 4348 * MiB
+    assert 64 * full == 8192 * MiB
+    # every step stays within C+1 full layers plus the rest streaming
+    for l, t in enumerate(acc["transient"]):
+        nf = min(l, 32) + 1
+        assert t == nf * full + (l + 1 - nf) * stream
