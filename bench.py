@@ -1,0 +1,314 @@
+"""Benchmark of the LightTransfer-Test hot path on one MI355X.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+
+Headline leg (the step): one LightTransfer-Test layer at the qwen32k shape
+(B1 N32768 Hq40 Hkv8 D128 bf16, keys of tokens 0..3 x3, S4 R1020 W128):
+causal GQA prefill with LSE and the lazy-ratio epilogue + per-head mean,
+ratios to the host, layer score into the lazy-layer queue, and the KV of the
+evicted layer compacted to its sink + recent slice.  value = algorithmic
+prefill + lazy-numerator FLOP per step / wall time per step.
+
+Other legs, reported beside it: the same prefill without the epilogue
+(lazy-ratio overhead), streaming attention on the same tensors, and one
+hybrid decode step at B8 / 100000-token context over 64 layers (32 full,
+32 streaming at 1024 rows; one distinct buffer per layer; the 64 calls are
+captured once in a HIP graph and replayed).
+
+roofline: the prefill+lazy kernel, FLOP per launch over its mean duration
+from HIP events on the launch stream, against the 2.5 PFLOP/s dense bf16
+matrix-core peak.  cpu_baseline: the fp64 oracle on a bounded row sample of
+the same workload, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 matrix-core peak, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E peak, B/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_flop(B, Hq, N, D):
+    return 4.0 * B * Hq * D * N * (N + 1) / 2
+
+
+def lazy_flop(B, Hq, N, D, S, R, W):
+    return 2.0 * B * Hq * D * sum(min(S + R, i + 1) for i in range(N - W, N))
+
+
+def streaming_flop(B, Hq, N, D, S, R):
+    K = S + R
+    # sum_i min(i+1, K)
+    tot = K * (K + 1) // 2 + max(0, N - K) * K if N >= K else N * (N + 1) // 2
+    return 4.0 * B * Hq * D * tot
+
+
+def traffic_from_profile(src_path: str, prof_path: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
+    if the summary is missing or the kernel source changed since."""
+    if not os.path.exists(prof_path):
+        return None
+    text = open(prof_path).read()
+    sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+    m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != sha:
+        return None
+    return float(m_b.group(1))
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=98304,
+                    help="rows of the oracle's CPU sample")
+    ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
+                    help="only run a device-to-device copy of BYTES, 5 times (the reference "
+                         "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the kernels run on one GPU's share; see DESIGN.md for how it would shard).",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from kv_cache_compression_causal_amd import _lib, api, ops, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    if not os.path.exists(_lib.LIB_PATH):
+        from kv_cache_compression_causal_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_only:
+        src = torch.empty(args.copy_only // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_only} bytes x5")
+        return 0
+    K, Wm = args.steps, args.warmup
+    w = synth.QWEN32K
+    B, N, Hq, Hkv, D, S, R, W = w.B, w.N, w.Hq, w.Hkv, w.D, w.S, w.R, w.W
+
+    log(f"generating {w.name} inputs on device")
+    q, k, v = synth.workload_qkv(w, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=dev, dtype=torch.float32)
+    rows = torch.empty(B, Hq, W, device=dev, dtype=torch.float32)
+    ratio = torch.empty(B, Hq, device=dev, dtype=torch.float32)
+    srows = min(N, S + R)
+    k_st = torch.empty(B, Hkv, srows, D, device=dev, dtype=q.dtype)
+    v_st = torch.empty_like(k_st)
+    sout = torch.empty_like(q)
+    slse = torch.empty_like(lse)
+    total_layers = K + Wm
+    queue = api.LazyQueue(total_layers, total_layers // 2)
+    stream = torch.cuda.current_stream()
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    layer = [0]
+
+    def step(timed_idx=None):
+        if timed_idx is not None:
+            ev0[timed_idx].record(stream)
+        api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, stream)
+        if timed_idx is not None:
+            ev1[timed_idx].record(stream)
+        r = ratio.cpu()  # the per-layer device->host sync of the method
+        score = float(r.double().mean())
+        evicted = queue.push(layer[0], score)
+        layer[0] += 1
+        if evicted >= 0:
+            # one resident layer stands in for every layer: compact it
+            api.lt_compact_kv_streaming(k, v, k_st, v_st, S, R, stream)
+
+    log("warmup")
+    for _ in range(Wm):
+        step()
+    torch.cuda.synchronize()
+    log(f"timing {K} steps")
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / K
+    fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
+    value = fl / (ms_step * 1e-3) / 1e12
+    achieved = fl / (kern_ms * 1e-3) / 1e12
+    log(f"prefill+lazy: {ms_step:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.1f} TFLOP/s")
+    queue.close()
+
+    # plain prefill (W = 0) for the lazy-ratio overhead
+    def timed(fn, reps):
+        for _ in range(Wm):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    plain_ms = timed(lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, 0, None, None, 0.0,
+                                                          stream), K)
+    log(f"plain prefill: {plain_ms:.3f} ms")
+    st_ms = timed(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, stream), K)
+    st_fl = streaming_flop(B, Hq, N, D, S, R)
+    log(f"streaming: {st_ms:.3f} ms, {st_fl / st_ms / 1e9:.1f} TFLOP/s")
+
+    result = {
+        "metric": "prefill attn+lazy-ratio TFLOP/s @32K (% MFMA peak); hybrid decode HBM GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": Wm,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen32k layer: B1 N32768 Hq40 Hkv8 D128 bf16, sink keys x3, "
+                               "S4 R1020 W128; step = prefill+LSE+lazy ratio, ratio D2H, "
+                               "queue push, KV compaction",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "prefill_lazy": {"kernel_ms": round(kern_ms, 4), "tflops": round(achieved, 2),
+                         "frac_mfma_peak": round(achieved * 1e12 / PEAK_BF16, 4),
+                         "flop_per_launch": fl},
+        "lazy_overhead_pct": round(100.0 * (kern_ms - plain_ms) / plain_ms, 3),
+        "prefill_plain": {"ms": round(plain_ms, 4),
+                          "tflops": round(prefill_flop(B, Hq, N, D) / plain_ms / 1e9, 2)},
+        "streaming": {"ms": round(st_ms, 4), "tflops": round(st_fl / st_ms / 1e9, 2),
+                      "flop": st_fl},
+    }
+
+    src = os.path.join(ROOT, "kv_cache_compression_causal_amd", "csrc", "attn_bf16.hip")
+    traffic = traffic_from_profile(src, os.path.join(ROOT, "profiles", "prefill_lazy_qwen32k_pmc.txt"))
+    result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
+                          "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
+                          "traffic": traffic,
+                          "kernel": "attn_bf16_kernel<D128,GC5,PB1,BN32,FULL_LAZY> + lazy_reduce"}
+    del sout, slse
+
+    # hybrid decode step: B8, context 100000, 64 layers (32 full + 32 streaming)
+    if not args.no_decode:
+        dw = synth.DECODE100K
+        L = int(dw.extra["layers"])
+        nfull = int(dw.extra["full_layers"])
+        log("allocating the 64-layer hybrid KV cache on device")
+        qs, ks_, vs_, outs, lses, lens = [], [], [], [], [], []
+        for l in range(L):
+            ql, kl, vl = synth.decode_layer(l, dw, device=dev)
+            qs.append(ql); ks_.append(kl); vs_.append(vl); lens.append(kl.shape[2])
+            outs.append(torch.empty_like(ql))
+            lses.append(torch.empty(dw.B, dw.Hq, device=dev, dtype=torch.float32))
+        ws = ops.decode_workspace(dw.B, dw.Hq, dw.Hkv, dw.D, max(lens), dev)
+        torch.cuda.synchronize()
+        bytes_step = sum(2 * dw.B * dw.Hkv * n * dw.D * 2 + 2 * dw.B * dw.Hq * dw.D * 2 for n in lens)
+
+        def decode_all(st):
+            for l in range(L):
+                api.lt_hybrid_decode_attn(qs[l], ks_[l], vs_[l], lens[l], outs[l], lses[l], ws, 0.0, st)
+
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            decode_all(cap)  # eager warm call on the capture stream
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            decode_all(cap)
+        torch.cuda.synchronize()
+        log("decode graph captured")
+        for _ in range(Wm):
+            graph.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(K):
+            graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        d_ms = a.elapsed_time(b) / K
+        gbps = bytes_step / (d_ms * 1e-3) / 1e9
+        log(f"decode: {d_ms:.3f} ms/step, {gbps:.1f} GB/s")
+        result["decode"] = {"workload": "decode100k: B8, context 100000, 64 layers Hq40 Hkv8 D128 "
+                                        "bf16, 32 full (100000 rows) + 32 streaming (1024 rows)",
+                            "ms_per_step": round(d_ms, 4), "gbps": round(gbps, 1),
+                            "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
+                            "bytes_per_step": bytes_step}
+        del graph, qs, ks_, vs_, outs, lses, ws
+        torch.cuda.empty_cache()
+
+    # CPU baseline: the oracle on a bounded row sample of the same workload
+    if not args.no_cpu:
+        import oracle
+        log("timing the oracle on a row sample")
+        nrow = args.cpu_rows
+        rng = np.random.default_rng(0)
+        G = Hq // Hkv
+        heads = rng.integers(0, Hq, size=nrow)
+        pos = np.concatenate([np.arange(N - W, N), rng.integers(0, N, size=nrow - W)])[:nrow]
+        kh_cache = {}
+        flop = 0.0
+        t_cpu = 0.0
+        for h in sorted(set(int(x) for x in heads)):
+            sel = np.nonzero(heads == h)[0]
+            hk = h // G
+            if hk not in kh_cache:
+                kh_cache[hk] = (k[0, hk].double().cpu().numpy(), v[0, hk].double().cpu().numpy())
+            kh, vh = kh_cache[hk]
+            ps = pos[sel].astype(np.int32)
+            qr = q[0, h].index_select(0, torch.as_tensor(ps, device=dev, dtype=torch.long)).double().cpu().numpy()
+            c0 = time.perf_counter()
+            oracle.rows(kh, vh, ps, qr, S=S, R=R, lazy=True, streaming=False)
+            t_cpu += time.perf_counter() - c0
+            flop += sum(4.0 * D * (int(p) + 1) for p in ps)
+            flop += sum(2.0 * D * min(S + R, int(p) + 1) for p in ps if p >= N - W)
+        cpu_tflops = flop / t_cpu / 1e12
+        result["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
+                                  "cores": oracle.threads(), "kind": "oracle",
+                                  "sample": f"{nrow} query rows of the qwen32k layer (the last W=128 rows "
+                                            f"+ uniform random rows, random heads), full softmax row "
+                                            f"materialised in fp64; {t_cpu:.1f} s; FLOP counted as "
+                                            f"for the GPU (4*D*(i+1) per row + lazy numerator)"}
+        log(f"oracle: {cpu_tflops * 1e3:.3f} GFLOP/s on {oracle.threads()} threads ({t_cpu:.1f} s)")
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,181 @@
+/*
+ * lt.h -- C ABI of the LightTransfer-Test hot path on MI355X (gfx950).
+ *
+ * LightTransfer-Test converts a dense transformer into a hybrid one during
+ * prefill: each layer's "lazy ratio" -- the softmax mass its last W queries
+ * put on the S initial (sink) keys plus each query's R most recent keys -- is
+ * measured as the layer runs, a priority queue keyed by that ratio keeps at
+ * most C layers at full KV, and every layer the queue evicts has its KV cut
+ * to the sink + recent slice and runs streaming attention from then on.
+ * Sources, by page and section:
+ *   [P1] Chinese write-up (xzbcqc.com): "problem 1 / solution 1" -- Flash
+ *        Attention stores no attention weights; its LSE is the ratio's
+ *        denominator and the numerator costs O(1) per query instead of an
+ *        O(seq_len) recompute.  "problem 2 / solution 2" -- the priority
+ *        queue that bounds peak prefill memory at 50% full KV + 50%
+ *        streaming KV by evicting the highest-ratio layer on overflow.
+ *   [P3] Press-release page (wuwenjie.xyz): "LightTransfer method" -- the
+ *        lazy ratio sums the attention weights from queries to the initial
+ *        and the recent keys.
+ *   [P4] LightTransfer project page: "Introduction" (lazy layers become
+ *        streaming attention with a constant-size KV cache); Figure 2 caption
+ *        (queue of (lazy ratio, layer index) updated after every layer; the
+ *        evicted layer's KV cache is reduced).
+ *
+ * Conventions shared by every call
+ *   Shapes: B batch, N sequence length (queries = keys, causal, aligned at
+ *   position 0: key j is visible to query i iff j <= i), Hq query heads, Hkv
+ *   KV heads with Hq % Hkv == 0 (query head h reads KV head h / (Hq/Hkv)),
+ *   D head dim (64 or 128).  The recent set of query i is (i-R, i], the sink
+ *   set [0, S).
+ *   Views: lt_view.data is a DEVICE pointer; sb, sh, sn are element strides of
+ *   the batch, head and row dims; the head dim is contiguous.  Data pointers
+ *   must be 16-byte aligned and strides multiples of 8 elements (bf16) or 4
+ *   (f32), so 128-bit loads are legal.
+ *   Ownership: the caller owns every buffer (device memory and workspace);
+ *   the library never allocates or frees device memory.
+ *   Streams: device calls are asynchronous on the given stream, never
+ *   synchronise, and write their outputs only; results are valid once the
+ *   stream reaches that point.
+ *   Errors: every argument is checked before anything is launched, so a
+ *   non-zero status leaves every output untouched.  lt_last_error() returns
+ *   the calling thread's last message.  Nothing throws or aborts.
+ */
+#ifndef LT_H
+#define LT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    LT_OK = 0,
+    LT_ERR_NULL = 1,      /* a required pointer is NULL */
+    LT_ERR_SHAPE = 2,     /* sizes out of range or inconsistent */
+    LT_ERR_DTYPE = 3,     /* unsupported dtype or head dim */
+    LT_ERR_LAYOUT = 4,    /* misaligned pointer or stride */
+    LT_ERR_WORKSPACE = 5, /* workspace too small */
+    LT_ERR_HIP = 6,       /* the HIP runtime reported an error at launch */
+    LT_ERR_VALUE = 7      /* bad value: NaN/inf score, capacity outside [0, L], layer out of order */
+};
+
+/* Element types. */
+enum { LT_F32 = 0, LT_BF16 = 1 };
+
+/* A strided [B, H, rows, D] tensor in device memory (element strides). */
+typedef struct {
+    void *data;
+    int64_t sb, sh, sn;
+} lt_view;
+
+/* Prefill problem shape.  scale <= 0 selects 1/sqrt(D). */
+typedef struct {
+    int B, N, Hq, Hkv, D;
+    int dtype; /* LT_F32 or LT_BF16; q, k, v and out share it */
+    float scale;
+} lt_shape;
+
+/*
+ * Causal GQA flash-attention prefill that also returns the per-row LSE and,
+ * in the same call, each head's lazy ratio ([P1] solution 1, [P3] method).
+ *   q [B,Hq,N,D], k/v [B,Hkv,N,D], out [B,Hq,N,D]: views as above.
+ *   lse [B,Hq,N] fp32, contiguous, natural log: ln sum_{j<=i} exp(s_ij),
+ *     s_ij = scale * q_i . k_j.  Required.
+ *   W == 0: plain prefill; lazy_rows/lazy_ratio are ignored (may be NULL).
+ *   W >= 1 (W <= N): lazy_rows [B,Hq,W] fp32 receives, for the last W
+ *     queries i = N-W..N-1, r_i = sum over keys j <= i with j < S or
+ *     j > i-R of exp(s_ij - lse_i); lazy_ratio [B,Hq] fp32 receives the mean
+ *     of the W values, summed in row order.  Both required.  The numerator is
+ *     taken after the main pass from the sink and recent key tiles only; the
+ *     denominator is the LSE just produced.
+ *   Needs S >= 0, R >= 1.  bf16 runs on the matrix cores (fp32 accumulate,
+ *   softmax weights rounded to bf16 for the P.V product); f32 runs in fp32.
+ */
+int lt_prefill_attn_lse_lazy(const lt_shape *shape, lt_view q, lt_view k, lt_view v,
+                             lt_view out, float *lse, int S, int R, int W, float *lazy_rows,
+                             float *lazy_ratio, hipStream_t stream);
+
+/*
+ * Streaming (sink + sliding-window) attention of converted layers ([P4]
+ * introduction; [P1] training paragraph): query i attends only to keys
+ * j <= i with j < S or j > i-R.  Same layouts as the prefill; lse [B,Hq,N]
+ * fp32 may be NULL.  Needs S >= 0, R >= 1.
+ */
+int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
+                      float *lse, int S, int R, hipStream_t stream);
+
+/*
+ * Workspace for lt_hybrid_decode_attn at these sizes, in bytes (0 is
+ * possible).  Host-only; no device call.
+ */
+int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len,
+                                     size_t *bytes);
+
+/*
+ * One decode step of one layer over its KV cache (full or streaming): the
+ * KV reduction the pages report is realised here ([P1] training paragraph,
+ * [P3] results).  q [B,Hq,D] contiguous (device), k_cache/v_cache views
+ * [B,Hkv,>=kv_len,D]; every one of the kv_len rows is attended (the cache
+ * includes the current token; row order is irrelevant).  A full layer passes
+ * its whole context; a streaming layer passes its S+R-row cache.
+ *   out [B,Hq,D] contiguous, same dtype as q; lse [B,Hq] fp32 or NULL.
+ *   ws: device workspace of at least lt_hybrid_decode_workspace_bytes().
+ */
+int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
+                          lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Switch a layer's KV to the streaming version ([P1] solution 2; [P4]
+ * Figure 2): copy rows [0,S) then [N-R,N) of every (b, kv head) of k_full /
+ * v_full [B,Hkv,N,D] into rows 0..S+R-1 of k_stream / v_stream
+ * [B,Hkv,>=S+R,D]; when N <= S+R all N rows are copied in order.  A byte
+ * copy; the caller frees the full buffers afterwards.
+ */
+int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream,
+                            int B, int Hkv, int N, int D, int dtype, int S, int R,
+                            hipStream_t stream);
+
+/*
+ * (full, streaming) KV bytes of one layer: 2*B*Hkv*N*D*e and
+ * 2*B*Hkv*min(N,S+R)*D*e, e the element size.  Host-only.
+ */
+int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64_t *full_bytes,
+                int64_t *stream_bytes);
+
+/*
+ * The lazy-layer priority queue ([P1] solution 2; [P4] Figure 2), online
+ * form: after layer `layer` finishes, push (score, layer); while the queue
+ * holds more than C layers, the one with the highest score leaves (equal
+ * scores: the lower layer index) and becomes a streaming layer.  *evicted
+ * receives that layer or -1.  Layers must be pushed in order 0..L-1.  Host
+ * memory is owned by the handle.
+ */
+typedef struct lt_lazy_queue lt_lazy_queue;
+int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out);
+int lt_lazy_queue_push(lt_lazy_queue *queue, int layer, double score, int *evicted);
+void lt_lazy_queue_destroy(lt_lazy_queue *queue);
+
+/*
+ * Batch form of the same queue.  head_ratio [L][n] host fp32: the n
+ * per-(batch, head) lazy ratios of each layer.  A layer's score is their
+ * mean, summed in fp64 in index order (written to layer_score [L] if not
+ * NULL).  Then L pushes as above: evicted_at_step [L] (-1 = none) and
+ * is_streaming [L] (0/1).  Host-only.
+ */
+int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
+                          int *evicted_at_step, uint8_t *is_streaming);
+
+/* Name of a status code, and the calling thread's last error message. */
+const char *lt_status_str(int status);
+const char *lt_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LT_H */

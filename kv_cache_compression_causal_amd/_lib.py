@@ -1,0 +1,99 @@
+"""ctypes loader for liblt.so: declares every exported symbol of include/lt.h.
+
+The library must exist (built by ``python -m kv_cache_compression_causal_amd.build``
+or ``__graft_entry__.build()``); there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblt.so")
+
+LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_LAYOUT, LT_ERR_WORKSPACE, LT_ERR_HIP, \
+    LT_ERR_VALUE = range(8)
+LT_F32, LT_BF16 = 0, 1
+
+# Every symbol include/lt.h declares.
+EXPORTS = (
+    "lt_prefill_attn_lse_lazy", "lt_streaming_attn", "lt_hybrid_decode_workspace_bytes",
+    "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
+    "lt_lazy_queue_push", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
+    "lt_last_error",
+)
+
+
+class LtView(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("sb", ctypes.c_int64), ("sh", ctypes.c_int64),
+                ("sn", ctypes.c_int64)]
+
+
+class LtShape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("N", ctypes.c_int), ("Hq", ctypes.c_int),
+                ("Hkv", ctypes.c_int), ("D", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("scale", ctypes.c_float)]
+
+
+class LtError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblt.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m kv_cache_compression_causal_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    c_int, c_int64, c_void_p, c_size_t = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
+    fp = ctypes.POINTER(ctypes.c_float)
+    L.lt_prefill_attn_lse_lazy.argtypes = [ctypes.POINTER(LtShape), LtView, LtView, LtView, LtView,
+                                           c_void_p, c_int, c_int, c_int, c_void_p, c_void_p, c_void_p]
+    L.lt_prefill_attn_lse_lazy.restype = c_int
+    L.lt_streaming_attn.argtypes = [ctypes.POINTER(LtShape), LtView, LtView, LtView, LtView,
+                                    c_void_p, c_int, c_int, c_void_p]
+    L.lt_streaming_attn.restype = c_int
+    L.lt_hybrid_decode_workspace_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int64,
+                                                   ctypes.POINTER(c_size_t)]
+    L.lt_hybrid_decode_workspace_bytes.restype = c_int
+    L.lt_hybrid_decode_attn.argtypes = [c_int, c_int, c_int, c_int, c_int, ctypes.c_float, c_void_p,
+                                        LtView, LtView, c_int64, c_void_p, c_void_p, c_void_p,
+                                        c_size_t, c_void_p]
+    L.lt_hybrid_decode_attn.restype = c_int
+    L.lt_compact_kv_streaming.argtypes = [LtView, LtView, LtView, LtView, c_int, c_int, c_int,
+                                          c_int, c_int, c_int, c_int, c_void_p]
+    L.lt_compact_kv_streaming.restype = c_int
+    L.lt_kv_bytes.argtypes = [c_int, c_int, c_int64, c_int, c_int, c_int, c_int,
+                              ctypes.POINTER(c_int64), ctypes.POINTER(c_int64)]
+    L.lt_kv_bytes.restype = c_int
+    L.lt_lazy_queue_create.argtypes = [c_int, c_int, ctypes.POINTER(c_void_p)]
+    L.lt_lazy_queue_create.restype = c_int
+    L.lt_lazy_queue_push.argtypes = [c_void_p, c_int, ctypes.c_double, ctypes.POINTER(c_int)]
+    L.lt_lazy_queue_push.restype = c_int
+    L.lt_lazy_queue_destroy.argtypes = [c_void_p]
+    L.lt_lazy_queue_destroy.restype = None
+    L.lt_select_lazy_layers.argtypes = [fp, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_uint8)]
+    L.lt_select_lazy_layers.restype = c_int
+    L.lt_status_str.argtypes = [c_int]
+    L.lt_status_str.restype = ctypes.c_char_p
+    L.lt_last_error.argtypes = []
+    L.lt_last_error.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def status_name(status: int) -> str:
+    return lib().lt_status_str(status).decode()
+
+
+def check(status: int) -> None:
+    if status != LT_OK:
+        raise LtError(status, lib().lt_last_error().decode())

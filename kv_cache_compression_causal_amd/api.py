@@ -1,0 +1,177 @@
+"""Thin Python binding of include/lt.h, one function per C entry point.
+
+Marshalling only: tensors become (device pointer, element strides), the
+stream is torch's current HIP stream unless one is given, and a non-zero
+status raises LtError.  Every step of the computation runs in liblt.so.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+from ._lib import LT_BF16, LT_F32, LtShape, LtView, check, lib
+
+_DTYPES = {torch.bfloat16: LT_BF16, torch.float32: LT_F32}
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _view(t: torch.Tensor) -> LtView:
+    """[B, H, rows, D] tensor -> lt_view (head dim must be contiguous)."""
+    if t.dim() != 4:
+        raise ValueError("expected a [B, H, rows, D] tensor")
+    if t.stride(3) != 1:
+        raise ValueError("head dim must be contiguous")
+    return LtView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _shape(q: torch.Tensor, k: torch.Tensor, scale: float) -> LtShape:
+    B, Hq, N, D = q.shape
+    return LtShape(B, N, Hq, k.shape[1], D, _dtype_code(q), float(scale))
+
+
+def _same_dtype(*ts: torch.Tensor) -> None:
+    if len({t.dtype for t in ts}) != 1:
+        raise TypeError("q, k, v and out must share one dtype")
+
+
+def lt_prefill_attn_lse_lazy(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                             lse: torch.Tensor, S: int, R: int, W: int,
+                             lazy_rows: Optional[torch.Tensor] = None,
+                             lazy_ratio: Optional[torch.Tensor] = None, scale: float = 0.0,
+                             stream=None) -> None:
+    _same_dtype(q, k, v, out)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, out")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    shp = _shape(q, k, scale)
+    check(lib().lt_prefill_attn_lse_lazy(ctypes.byref(shp), _view(q), _view(k), _view(v), _view(out),
+                                         _ptr(lse), S, R, W, _ptr(lazy_rows), _ptr(lazy_ratio),
+                                         _stream(stream)))
+
+
+def lt_streaming_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                      lse: Optional[torch.Tensor], S: int, R: int, scale: float = 0.0,
+                      stream=None) -> None:
+    _same_dtype(q, k, v, out)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, out")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    shp = _shape(q, k, scale)
+    check(lib().lt_streaming_attn(ctypes.byref(shp), _view(q), _view(k), _view(v), _view(out),
+                                  _ptr(lse), S, R, _stream(stream)))
+
+
+def lt_hybrid_decode_workspace_bytes(B: int, Hq: int, Hkv: int, D: int, kv_len: int) -> int:
+    n = ctypes.c_size_t()
+    check(lib().lt_hybrid_decode_workspace_bytes(B, Hq, Hkv, D, kv_len, ctypes.byref(n)))
+    return n.value
+
+
+def lt_hybrid_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          kv_len: int, out: torch.Tensor, lse: Optional[torch.Tensor],
+                          ws: torch.Tensor, scale: float = 0.0, stream=None) -> None:
+    """q, out [B, Hq, D] contiguous; caches [B, Hkv, >=kv_len, D]; ws from
+    lt_hybrid_decode_workspace_bytes (any dtype, contiguous)."""
+    if not (q.is_contiguous() and out.is_contiguous() and ws.is_contiguous()):
+        raise ValueError("q, out and ws must be contiguous")
+    _same_dtype(q, k_cache, v_cache, out)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or k_cache.shape[0] != B or k_cache.shape[3] != D \
+            or k_cache.shape[2] < kv_len or v_cache.shape[:2] != k_cache.shape[:2] \
+            or v_cache.shape[2] < kv_len or v_cache.shape[3] != D:
+        raise ValueError("decode shape mismatch")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    check(lib().lt_hybrid_decode_attn(B, Hq, k_cache.shape[1], D, _dtype_code(q), float(scale),
+                                      q.data_ptr(), _view(k_cache), _view(v_cache), int(kv_len),
+                                      out.data_ptr(), _ptr(lse), ws.data_ptr(),
+                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def lt_compact_kv_streaming(k_full: torch.Tensor, v_full: torch.Tensor, k_stream: torch.Tensor,
+                            v_stream: torch.Tensor, S: int, R: int, stream=None) -> None:
+    B, Hkv, N, D = k_full.shape
+    rows = min(N, S + R)
+    for t in (v_full,):
+        if t.shape != k_full.shape:
+            raise ValueError("k_full / v_full shape mismatch")
+    for t in (k_stream, v_stream):
+        if t.shape[0] != B or t.shape[1] != Hkv or t.shape[2] < rows or t.shape[3] != D:
+            raise ValueError("streaming cache too small")
+    _same_dtype(k_full, v_full, k_stream, v_stream)
+    check(lib().lt_compact_kv_streaming(_view(k_full), _view(v_full), _view(k_stream),
+                                        _view(v_stream), B, Hkv, N, D, _dtype_code(k_full), S, R,
+                                        _stream(stream)))
+
+
+def lt_kv_bytes(B: int, Hkv: int, N: int, D: int, dtype: int, S: int, R: int) -> Tuple[int, int]:
+    full, stream = ctypes.c_int64(), ctypes.c_int64()
+    check(lib().lt_kv_bytes(B, Hkv, N, D, dtype, S, R, ctypes.byref(full), ctypes.byref(stream)))
+    return full.value, stream.value
+
+
+class LazyQueue:
+    """lt_lazy_queue_create / _push / _destroy."""
+
+    def __init__(self, L: int, C: int):
+        h = ctypes.c_void_p()
+        check(lib().lt_lazy_queue_create(L, C, ctypes.byref(h)))
+        self._h = h
+
+    def push(self, layer: int, score: float) -> int:
+        ev = ctypes.c_int()
+        check(lib().lt_lazy_queue_push(self._h, layer, float(score), ctypes.byref(ev)))
+        return ev.value
+
+    def close(self) -> None:
+        if self._h:
+            lib().lt_lazy_queue_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def lt_select_lazy_layers(head_ratio, C: int):
+    """head_ratio [L, n] (host, fp32).  Returns (layer_score [L] float64,
+    evicted_at_step [L] int32, is_streaming [L] uint8)."""
+    hr = np.ascontiguousarray(np.asarray(head_ratio, dtype=np.float32))
+    if hr.ndim != 2:
+        raise ValueError("head_ratio must be [L, n]")
+    L, n = hr.shape
+    score = np.empty(L, dtype=np.float64)
+    ev = np.empty(L, dtype=np.int32)
+    st = np.empty(L, dtype=np.uint8)
+    check(lib().lt_select_lazy_layers(
+        hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), L, n, C,
+        score.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+        ev.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+        st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
+    return score, ev, st

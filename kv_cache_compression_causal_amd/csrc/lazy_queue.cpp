@@ -1,0 +1,146 @@
+// Lazy-layer priority queue (LightTransfer pages: Chinese write-up,
+// "solution 2"; project page, Figure 2 caption).  After each layer of the
+// prefill its (lazy ratio, layer index) enters the queue; while more than C
+// layers are queued, the laziest (highest ratio) leaves and its KV cache is
+// switched to the streaming version.  This bounds the prefill's KV at C full
+// layers plus streaming layers at every step.
+//
+// Readings the pages leave open: the queue pushes, then pops while its size
+// exceeds C (so the current layer may leave at its own step); equal ratios
+// evict the lower layer index first; a layer's score is the fp64 mean of its
+// per-(batch, head) ratios in index order.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "lt.h"
+
+extern "C" const char *lt_last_error(void);
+
+namespace {
+
+struct Entry {
+    double score;
+    int layer;
+};
+
+// "a ranks above b" in the max-heap: higher score, then lower layer index.
+inline bool above(const Entry &a, const Entry &b) {
+    return a.score > b.score || (a.score == b.score && a.layer < b.layer);
+}
+
+}  // namespace
+
+struct lt_lazy_queue {
+    int L, C, next;
+    std::vector<Entry> heap;  // binary max-heap under above()
+
+    void push(const Entry &e) {
+        heap.push_back(e);
+        size_t i = heap.size() - 1;
+        while (i > 0) {
+            size_t p = (i - 1) / 2;
+            if (!above(heap[i], heap[p])) break;
+            Entry t = heap[i]; heap[i] = heap[p]; heap[p] = t;
+            i = p;
+        }
+    }
+    Entry pop() {
+        Entry top = heap[0];
+        heap[0] = heap.back();
+        heap.pop_back();
+        size_t i = 0, n = heap.size();
+        for (;;) {
+            size_t l = 2 * i + 1, r = l + 1, best = i;
+            if (l < n && above(heap[l], heap[best])) best = l;
+            if (r < n && above(heap[r], heap[best])) best = r;
+            if (best == i) break;
+            Entry t = heap[i]; heap[i] = heap[best]; heap[best] = t;
+            i = best;
+        }
+        return top;
+    }
+};
+
+namespace {
+// Shares the thread-local error text of lt_api.cpp through a tiny setter.
+int qfail(int code, const char *msg);
+}  // namespace
+
+extern "C" {
+
+int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out) {
+    if (out == nullptr) return qfail(LT_ERR_NULL, "out is NULL");
+    if (L < 1) return qfail(LT_ERR_SHAPE, "L must be >= 1");
+    if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
+    lt_lazy_queue *q = new (std::nothrow) lt_lazy_queue();
+    if (q == nullptr) return qfail(LT_ERR_VALUE, "out of host memory");
+    q->L = L; q->C = C; q->next = 0;
+    q->heap.reserve((size_t)C + 1);
+    *out = q;
+    return qfail(LT_OK, "");
+}
+
+int lt_lazy_queue_push(lt_lazy_queue *q, int layer, double score, int *evicted) {
+    if (q == nullptr || evicted == nullptr) return qfail(LT_ERR_NULL, "queue/evicted is NULL");
+    if (layer != q->next) return qfail(LT_ERR_VALUE, "layers must be pushed in order");
+    if (isnan(score) || isinf(score)) return qfail(LT_ERR_VALUE, "score must be finite");
+    q->push(Entry{score, layer});
+    q->next++;
+    *evicted = -1;
+    if ((int)q->heap.size() > q->C) *evicted = q->pop().layer;
+    return qfail(LT_OK, "");
+}
+
+void lt_lazy_queue_destroy(lt_lazy_queue *q) { delete q; }
+
+int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
+                          int *evicted_at_step, uint8_t *is_streaming) {
+    if (head_ratio == nullptr || evicted_at_step == nullptr || is_streaming == nullptr)
+        return qfail(LT_ERR_NULL, "NULL argument");
+    if (L < 1 || n < 1) return qfail(LT_ERR_SHAPE, "L and n must be >= 1");
+    if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
+    std::vector<double> score((size_t)L);
+    for (int l = 0; l < L; ++l) {
+        double acc = 0.0;
+        for (int i = 0; i < n; ++i) {
+            const float x = head_ratio[(size_t)l * n + i];
+            if (isnan(x) || isinf(x)) return qfail(LT_ERR_VALUE, "head ratio is not finite");
+            acc += (double)x;
+        }
+        score[l] = acc / (double)n;
+    }
+    lt_lazy_queue q;
+    q.L = L; q.C = C; q.next = 0;
+    q.heap.reserve((size_t)C + 1);
+    for (int l = 0; l < L; ++l) is_streaming[l] = 0;
+    for (int l = 0; l < L; ++l) {
+        q.push(Entry{score[l], l});
+        evicted_at_step[l] = -1;
+        if ((int)q.heap.size() > C) {
+            const int v = q.pop().layer;
+            evicted_at_step[l] = v;
+            is_streaming[v] = 1;
+        }
+    }
+    if (layer_score != nullptr)
+        for (int l = 0; l < L; ++l) layer_score[l] = score[l];
+    return qfail(LT_OK, "");
+}
+
+}  // extern "C"
+
+namespace lt_detail {
+void set_error(const char *msg);
+}
+
+namespace {
+int qfail(int code, const char *msg) {
+    lt_detail::set_error(msg);
+    return code;
+}
+}  // namespace

@@ -1,0 +1,216 @@
+// C-ABI shim: argument validation, launch configuration and status codes.
+// Every check runs before the first launch, so a failing call writes nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "lt.h"
+#include "lt_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return LT_OK;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(LT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+int elem_size(int dtype) { return dtype == LT_BF16 ? 2 : dtype == LT_F32 ? 4 : 0; }
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// A [B, H, rows, D] view: pointer, alignment and stride checks.
+int check_view(const lt_view &v, const char *name, int dtype) {
+    if (v.data == nullptr) return fail(LT_ERR_NULL, "%s.data is NULL", name);
+    if (!aligned16(v.data)) return fail(LT_ERR_LAYOUT, "%s.data is not 16-byte aligned", name);
+    const int64_t m = dtype == LT_BF16 ? 8 : 4;
+    if (v.sb < 0 || v.sh < 0 || v.sn < 0 || v.sb % m || v.sh % m || v.sn % m)
+        return fail(LT_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) must be non-negative multiples of %lld",
+                    name, (long long)v.sb, (long long)v.sh, (long long)v.sn, (long long)m);
+    return LT_OK;
+}
+
+int check_shape(const lt_shape *s) {
+    if (s == nullptr) return fail(LT_ERR_NULL, "shape is NULL");
+    if (s->dtype != LT_F32 && s->dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", s->dtype);
+    if (s->D != 64 && s->D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", s->D);
+    if (s->B < 1 || s->N < 1 || s->Hq < 1 || s->Hkv < 1)
+        return fail(LT_ERR_SHAPE, "B, N, Hq, Hkv must be >= 1 (got %d, %d, %d, %d)", s->B, s->N, s->Hq, s->Hkv);
+    if (s->Hq % s->Hkv != 0) return fail(LT_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", s->Hq, s->Hkv);
+    if ((int64_t)s->N * 64 > INT32_MAX) return fail(LT_ERR_SHAPE, "N %d too large", s->N);
+    if (!(s->scale == s->scale) || isinf(s->scale)) return fail(LT_ERR_VALUE, "scale is not finite");
+    return LT_OK;
+}
+
+lt::AttnArgs make_args(const lt_shape *s, const lt_view &q, const lt_view &k, const lt_view &v,
+                       const lt_view &out, float *lse, int S, int R, int W, float *lazy_rows) {
+    lt::AttnArgs a{};
+    a.q = q.data; a.k = k.data; a.v = v.data; a.o = out.data;
+    a.lse = lse; a.lazy_rows = lazy_rows;
+    a.q_sb = q.sb; a.q_sh = q.sh; a.q_sn = q.sn;
+    a.k_sb = k.sb; a.k_sh = k.sh; a.k_sn = k.sn;
+    a.v_sb = v.sb; a.v_sh = v.sh; a.v_sn = v.sn;
+    a.o_sb = out.sb; a.o_sh = out.sh; a.o_sn = out.sn;
+    a.B = s->B; a.N = s->N; a.Hq = s->Hq; a.Hkv = s->Hkv; a.G = s->Hq / s->Hkv;
+    a.n_chunks = 1; a.n_qtiles = 1;
+    a.scale = s->scale > 0.f ? s->scale : 1.f / sqrtf((float)s->D);
+    a.c = a.scale * 1.4426950408889634f;
+    a.S = S; a.R = R; a.W = W;
+    return a;
+}
+
+}  // namespace
+
+namespace lt_detail {
+void set_error(const char *msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
+}  // namespace lt_detail
+
+extern "C" {
+
+const char *lt_status_str(int status) {
+    switch (status) {
+    case LT_OK: return "LT_OK";
+    case LT_ERR_NULL: return "LT_ERR_NULL";
+    case LT_ERR_SHAPE: return "LT_ERR_SHAPE";
+    case LT_ERR_DTYPE: return "LT_ERR_DTYPE";
+    case LT_ERR_LAYOUT: return "LT_ERR_LAYOUT";
+    case LT_ERR_WORKSPACE: return "LT_ERR_WORKSPACE";
+    case LT_ERR_HIP: return "LT_ERR_HIP";
+    case LT_ERR_VALUE: return "LT_ERR_VALUE";
+    default: return "LT_ERR_UNKNOWN";
+    }
+}
+
+const char *lt_last_error(void) { return g_err; }
+
+int lt_prefill_attn_lse_lazy(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
+                             float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio,
+                             hipStream_t stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
+        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
+        return e;
+    if (lse == nullptr) return fail(LT_ERR_NULL, "lse is NULL");
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    if (W < 0 || W > shape->N) return fail(LT_ERR_SHAPE, "W %d outside [0, N=%d]", W, shape->N);
+    if (W > 0 && (lazy_rows == nullptr || lazy_ratio == nullptr))
+        return fail(LT_ERR_NULL, "W > 0 needs lazy_rows and lazy_ratio");
+    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, W, lazy_rows);
+    const int mode = W > 0 ? lt::MODE_FULL_LAZY : lt::MODE_FULL;
+    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, mode, stream)
+                                            : lt::launch_attn_f32(a, shape->D, mode, stream);
+    if (he != hipSuccess) return hip_status(he, "prefill launch");
+    if (W > 0) {
+        he = lt::launch_lazy_reduce(lazy_rows, lazy_ratio, shape->B * shape->Hq, W, stream);
+        if (he != hipSuccess) return hip_status(he, "lazy reduce launch");
+    }
+    return ok();
+}
+
+int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
+                      float *lse, int S, int R, hipStream_t stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
+        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
+        return e;
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, 0, nullptr);
+    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, lt::MODE_STREAM, stream)
+                                            : lt::launch_attn_f32(a, shape->D, lt::MODE_STREAM, stream);
+    if (he != hipSuccess) return hip_status(he, "streaming launch");
+    return ok();
+}
+
+int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len, size_t *bytes) {
+    if (bytes == nullptr) return fail(LT_ERR_NULL, "bytes is NULL");
+    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
+        return fail(LT_ERR_SHAPE, "bad decode sizes");
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    *bytes = lt::decode_ws_bytes(B, Hq, D, lt::decode_num_splits(B, Hkv, kv_len));
+    return ok();
+}
+
+int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
+                          lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
+        return fail(LT_ERR_SHAPE, "bad decode sizes (B=%d Hq=%d Hkv=%d kv_len=%lld)", B, Hq, Hkv, (long long)kv_len);
+    if (dtype == LT_BF16 && Hq / Hkv > 16) return fail(LT_ERR_SHAPE, "bf16 decode supports Hq/Hkv <= 16");
+    if (kv_len > ((int64_t)1 << 40)) return fail(LT_ERR_SHAPE, "kv_len too large");
+    if (!(scale == scale) || isinf(scale)) return fail(LT_ERR_VALUE, "scale is not finite");
+    if (q == nullptr || out == nullptr) return fail(LT_ERR_NULL, "q/out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(LT_ERR_LAYOUT, "q/out not 16-byte aligned");
+    int e;
+    if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
+    const int n_splits = lt::decode_num_splits(B, Hkv, kv_len);
+    const size_t need = lt::decode_ws_bytes(B, Hq, D, n_splits);
+    if (ws == nullptr) return fail(LT_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(LT_ERR_LAYOUT, "workspace not 16-byte aligned");
+    if (ws_bytes < need) return fail(LT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    lt::DecodeArgs a{};
+    a.q = q; a.k = k_cache.data; a.v = v_cache.data;
+    a.k_sb = k_cache.sb; a.k_sh = k_cache.sh; a.k_sn = k_cache.sn;
+    a.v_sb = v_cache.sb; a.v_sh = v_cache.sh; a.v_sn = v_cache.sn;
+    a.o = out; a.lse = lse; a.ws = (float *)ws;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+    a.kv_len = kv_len; a.n_splits = n_splits;
+    a.keys_per_split = (kv_len + n_splits - 1) / n_splits;
+    a.keys_per_split = (a.keys_per_split + 63) / 64 * 64;
+    a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
+    a.c = a.scale * 1.4426950408889634f;
+    return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
+}
+
+int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, int B,
+                            int Hkv, int N, int D, int dtype, int S, int R, hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hkv < 1 || N < 1) return fail(LT_ERR_SHAPE, "B, Hkv, N must be >= 1");
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1");
+    int e;
+    if ((e = check_view(k_full, "k_full", dtype)) || (e = check_view(v_full, "v_full", dtype)) ||
+        (e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype)))
+        return e;
+    lt::CompactArgs a{};
+    a.kf = k_full.data; a.vf = v_full.data; a.ks = k_stream.data; a.vs = v_stream.data;
+    a.kf_sb = k_full.sb; a.kf_sh = k_full.sh; a.kf_sn = k_full.sn;
+    a.vf_sb = v_full.sb; a.vf_sh = v_full.sh; a.vf_sn = v_full.sn;
+    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
+    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
+    a.B = B; a.Hkv = Hkv; a.N = N; a.D = D; a.elem = elem_size(dtype); a.S = S; a.R = R;
+    a.rows_out = N <= S + R ? N : S + R;
+    return hip_status(lt::launch_compact(a, stream), "compaction launch");
+}
+
+int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64_t *full_bytes,
+                int64_t *stream_bytes) {
+    if (full_bytes == nullptr || stream_bytes == nullptr) return fail(LT_ERR_NULL, "output is NULL");
+    const int e = elem_size(dtype);
+    if (e == 0) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (B < 1 || Hkv < 1 || N < 1 || D < 1 || S < 0 || R < 0) return fail(LT_ERR_SHAPE, "bad sizes");
+    const int64_t rows = N < (int64_t)S + R ? N : (int64_t)S + R;
+    *full_bytes = 2 * (int64_t)B * Hkv * N * D * e;
+    *stream_bytes = 2 * (int64_t)B * Hkv * rows * D * e;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,72 @@
+// Internal declarations shared by the kernels and the C-ABI shim (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lt.h"
+
+namespace lt {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+// Attention kernel variants.
+enum Mode : int {
+    MODE_FULL = 0,       // causal attention + LSE
+    MODE_FULL_LAZY = 1,  // causal attention + LSE + lazy-ratio epilogue
+    MODE_STREAM = 2      // sink + recent attention (+ optional LSE)
+};
+
+struct AttnArgs {
+    const void *q, *k, *v;
+    void *o;
+    float *lse;        // [B,Hq,N] or nullptr (streaming only)
+    float *lazy_rows;  // [B,Hq,W] (lazy mode)
+    int64_t q_sb, q_sh, q_sn;
+    int64_t k_sb, k_sh, k_sn;
+    int64_t v_sb, v_sh, v_sn;
+    int64_t o_sb, o_sh, o_sn;
+    int B, N, Hq, Hkv, G;
+    int n_chunks;   // query heads of a group are split into n_chunks chunks
+    int n_qtiles;   // query tiles per (b, kv head, chunk)
+    float scale;    // softmax scale
+    float c;        // scale * log2(e)
+    int S, R, W;
+};
+
+// Launchers (return hipError_t of the launch).
+hipError_t launch_attn_bf16(const AttnArgs &a, int D, int mode, hipStream_t st);
+hipError_t launch_attn_f32(const AttnArgs &a, int D, int mode, hipStream_t st);
+hipError_t launch_lazy_reduce(const float *lazy_rows, float *lazy_ratio, int BH, int W,
+                              hipStream_t st);
+
+struct DecodeArgs {
+    const void *q;  // [B,Hq,D]
+    const void *k, *v;
+    int64_t k_sb, k_sh, k_sn, v_sb, v_sh, v_sn;
+    void *o;        // [B,Hq,D]
+    float *lse;     // [B,Hq] or nullptr
+    float *ws;      // partials
+    int B, Hq, Hkv, G, D;
+    int64_t kv_len;
+    int n_splits;
+    int64_t keys_per_split;
+    float scale, c;
+};
+int decode_num_splits(int B, int Hkv, int64_t kv_len);
+size_t decode_ws_bytes(int B, int Hq, int D, int n_splits);
+hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st);
+
+struct CompactArgs {
+    const void *kf, *vf;
+    void *ks, *vs;
+    int64_t kf_sb, kf_sh, kf_sn, vf_sb, vf_sh, vf_sn;
+    int64_t ks_sb, ks_sh, ks_sn, vs_sb, vs_sh, vs_sn;
+    int B, Hkv, N, D, elem, S, R, rows_out;
+};
+hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
+
+}  // namespace lt

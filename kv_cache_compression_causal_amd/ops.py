@@ -1,0 +1,59 @@
+"""Allocating conveniences over the C-ABI binding (outputs are new tensors on
+the inputs' device; every computation happens in liblt.so)."""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import api
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int, R: int, W: int,
+            scale: float = 0.0, stream=None):
+    """Returns (out, lse, lazy_rows, lazy_ratio); the last two are None if W == 0."""
+    B, Hq, N, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+    rows = ratio = None
+    if W > 0:
+        rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+        ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, scale, stream)
+    return out, lse, rows, ratio
+
+
+def streaming(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int, R: int,
+              with_lse: bool = True, scale: float = 0.0, stream=None):
+    B, Hq, N, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32) if with_lse else None
+    api.lt_streaming_attn(q, k, v, out, lse, S, R, scale, stream)
+    return out, lse
+
+
+def decode_workspace(B: int, Hq: int, Hkv: int, D: int, kv_len: int, device) -> torch.Tensor:
+    n = api.lt_hybrid_decode_workspace_bytes(B, Hq, Hkv, D, kv_len)
+    return torch.empty(max(n, 16), device=device, dtype=torch.uint8)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           kv_len: Optional[int] = None, ws: Optional[torch.Tensor] = None, scale: float = 0.0,
+           stream=None):
+    B, Hq, D = q.shape
+    L = k_cache.shape[2] if kv_len is None else kv_len
+    if ws is None:
+        ws = decode_workspace(B, Hq, k_cache.shape[1], D, L, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    api.lt_hybrid_decode_attn(q, k_cache, v_cache, L, out, lse, ws, scale, stream)
+    return out, lse
+
+
+def compact(k_full: torch.Tensor, v_full: torch.Tensor, S: int, R: int, stream=None):
+    B, Hkv, N, D = k_full.shape
+    rows = min(N, S + R)
+    ks = torch.empty(B, Hkv, rows, D, device=k_full.device, dtype=k_full.dtype)
+    vs = torch.empty_like(ks)
+    api.lt_compact_kv_streaming(k_full, v_full, ks, vs, S, R, stream)
+    return ks, vs

@@ -76,6 +76,8 @@ def load_library(path: str):
     lib.lto_decode.argtypes = [ctypes.c_int] * 4 + [ctypes.c_double, dp, dp, dp,
                                                      ctypes.c_long, dp, dp]
     lib.lto_decode.restype = ctypes.c_int
+    lib.lto_threads.argtypes = []
+    lib.lto_threads.restype = ctypes.c_int
     return lib
 
 
@@ -86,6 +88,11 @@ def _load():
             build()
         _lib = load_library(_LIB)
     return _lib
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().lto_threads())
 
 
 def _f64(a) -> np.ndarray:

@@ -40,6 +40,7 @@
  * and the invariants listed there.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -248,3 +249,6 @@ int lto_decode(int B, int Hq, int Hkv, int D, double scale, const double *q, con
     }
     return err ? LTO_NO_MEM : LTO_OK;
 }
+
+/* Threads an OpenMP region of the oracle uses (reported with its timings). */
+int lto_threads(void) { return omp_get_max_threads(); }

@@ -1,0 +1,184 @@
+"""C-ABI contract, on the CPU (no GPU needed, no kernel launched).
+
+* liblt.so loads and exports every function include/lt.h declares;
+* every validation error returns its status before anything is launched;
+* the host-side lazy-layer queue and KV accounting agree bit for bit with
+  the oracle on the same fp32 inputs.
+"""
+import ctypes
+import math
+import os
+import random
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_compression_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lt.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(_lib.LIB_PATH):
+        from kv_cache_compression_causal_amd import build
+        build.build()
+    return _lib.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return set(re.findall(r"\b(lt_[a-z0-9_]+)\s*\(", text))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert names == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+V = _lib.LtView
+GOOD = 0x100000  # aligned stand-in pointer; never dereferenced (validation fails first)
+
+
+def view(ptr=GOOD, sb=1 << 20, sh=1 << 16, sn=128):
+    return V(ptr, sb, sh, sn)
+
+
+def shape(**kw):
+    d = dict(B=1, N=64, Hq=4, Hkv=2, D=128, dtype=_lib.LT_BF16, scale=0.0)
+    d.update(kw)
+    return _lib.LtShape(**d)
+
+
+def prefill(L, shp, q=None, k=None, v=None, o=None, lse=GOOD, S=4, R=8, W=4, rows=GOOD, ratio=GOOD):
+    return L.lt_prefill_attn_lse_lazy(ctypes.byref(shp) if shp is not None else None,
+                                      q or view(), k or view(), v or view(), o or view(),
+                                      lse, S, R, W, rows, ratio, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=7), _lib.LT_ERR_DTYPE),
+    (dict(D=96), _lib.LT_ERR_DTYPE),
+    (dict(Hq=5, Hkv=2), _lib.LT_ERR_SHAPE),
+    (dict(N=0), _lib.LT_ERR_SHAPE),
+    (dict(B=0), _lib.LT_ERR_SHAPE),
+    (dict(scale=float("nan")), _lib.LT_ERR_VALUE),
+    (dict(scale=float("inf")), _lib.LT_ERR_VALUE),
+])
+def test_prefill_shape_errors(L, kw, code):
+    assert prefill(L, shape(**kw)) == code
+    assert L.lt_last_error().decode() != ""
+
+
+def test_prefill_argument_errors(L):
+    s = shape()
+    assert prefill(L, None) == _lib.LT_ERR_NULL
+    assert prefill(L, s, q=view(ptr=0)) == _lib.LT_ERR_NULL
+    assert prefill(L, s, k=view(ptr=GOOD + 2)) == _lib.LT_ERR_LAYOUT
+    assert prefill(L, s, v=view(sn=130)) == _lib.LT_ERR_LAYOUT
+    assert prefill(L, s, o=view(sb=-8)) == _lib.LT_ERR_LAYOUT
+    assert prefill(L, s, lse=None) == _lib.LT_ERR_NULL
+    assert prefill(L, s, W=65) == _lib.LT_ERR_SHAPE
+    assert prefill(L, s, W=-1) == _lib.LT_ERR_SHAPE
+    assert prefill(L, s, R=0) == _lib.LT_ERR_SHAPE
+    assert prefill(L, s, S=-1) == _lib.LT_ERR_SHAPE
+    assert prefill(L, s, rows=None) == _lib.LT_ERR_NULL
+    assert prefill(L, s, ratio=None) == _lib.LT_ERR_NULL
+    # fp32 allows strides that are multiples of 4 elements
+    assert prefill(L, shape(dtype=_lib.LT_F32), v=view(sn=132), R=0) == _lib.LT_ERR_SHAPE
+
+
+def test_streaming_errors(L):
+    s = shape()
+    f = L.lt_streaming_attn
+    assert f(None, view(), view(), view(), view(), None, 4, 8, None) == _lib.LT_ERR_NULL
+    assert f(ctypes.byref(s), view(), view(), view(), view(), None, 4, 0, None) == _lib.LT_ERR_SHAPE
+    assert f(ctypes.byref(s), view(ptr=GOOD + 8), view(), view(), view(), None, 4, 8, None) == _lib.LT_ERR_LAYOUT
+
+
+def test_decode_errors(L):
+    n = ctypes.c_size_t()
+    assert L.lt_hybrid_decode_workspace_bytes(8, 40, 8, 128, 100000, ctypes.byref(n)) == 0
+    need = n.value
+    assert need > 0
+    f = L.lt_hybrid_decode_attn
+    args = lambda **kw: dict(dict(B=8, Hq=40, Hkv=8, D=128, dt=_lib.LT_BF16, sc=0.0, q=GOOD, k=view(),
+                                  v=view(), L=100000, o=GOOD, lse=None, ws=GOOD, wsb=need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["B"], a["Hq"], a["Hkv"], a["D"], a["dt"], a["sc"], a["q"], a["k"], a["v"], a["L"],
+                 a["o"], a["lse"], a["ws"], a["wsb"], None)
+    assert call(wsb=need - 1) == _lib.LT_ERR_WORKSPACE
+    assert call(ws=None) == _lib.LT_ERR_NULL
+    assert call(Hq=34, Hkv=2) == _lib.LT_ERR_SHAPE        # G = 17 > 16
+    assert call(Hq=41) == _lib.LT_ERR_SHAPE
+    assert call(L=0) == _lib.LT_ERR_SHAPE
+    assert call(D=80) == _lib.LT_ERR_DTYPE
+    assert call(dt=3) == _lib.LT_ERR_DTYPE
+    assert call(q=GOOD + 4) == _lib.LT_ERR_LAYOUT
+    assert call(k=view(sn=100)) == _lib.LT_ERR_LAYOUT
+    assert call(sc=float("nan")) == _lib.LT_ERR_VALUE
+
+
+def test_compact_errors(L):
+    f = L.lt_compact_kv_streaming
+    assert f(view(), view(), view(), view(), 1, 8, 100, 128, _lib.LT_BF16, 4, 0, None) == _lib.LT_ERR_SHAPE
+    assert f(view(), view(), view(ptr=0), view(), 1, 8, 100, 128, _lib.LT_BF16, 4, 10, None) == _lib.LT_ERR_NULL
+    assert f(view(), view(), view(), view(), 1, 8, 100, 48, _lib.LT_BF16, 4, 10, None) == _lib.LT_ERR_DTYPE
+
+
+def test_status_strings(L):
+    assert [L.lt_status_str(i).decode() for i in range(8)] == [
+        "LT_OK", "LT_ERR_NULL", "LT_ERR_SHAPE", "LT_ERR_DTYPE", "LT_ERR_LAYOUT", "LT_ERR_WORKSPACE",
+        "LT_ERR_HIP", "LT_ERR_VALUE"]
+
+
+@pytest.mark.parametrize("seed", range(50))
+def test_select_matches_oracle_bit_exact(L, seed):
+    from kv_cache_compression_causal_amd import api
+    rnd = random.Random(seed)
+    Lyr = rnd.randint(1, 64)
+    n = rnd.randint(1, 40)
+    C = rnd.randint(0, Lyr)
+    hr = np.array([[rnd.choice([rnd.random(), 0.5, 0.25]) for _ in range(n)] for _ in range(Lyr)],
+                  dtype=np.float32)
+    score, ev, st = api.lt_select_lazy_layers(hr, C)
+    want_scores = [oracle.layer_score(row.astype(np.float64)) for row in hr]
+    assert list(score) == want_scores
+    wev, wst = oracle.select_lazy_layers(want_scores, C)
+    assert list(ev) == wev and list(st) == wst
+    q = api.LazyQueue(Lyr, C)
+    assert [q.push(l, s) for l, s in enumerate(want_scores)] == wev
+    q.close()
+
+
+def test_queue_errors(L):
+    from kv_cache_compression_causal_amd import api
+    with pytest.raises(_lib.LtError) as e:
+        api.lt_select_lazy_layers(np.array([[0.1], [float("nan")]], dtype=np.float32), 1)
+    assert e.value.status == _lib.LT_ERR_VALUE
+    with pytest.raises(_lib.LtError):
+        api.lt_select_lazy_layers(np.zeros((3, 2), dtype=np.float32), 4)
+    q = api.LazyQueue(3, 1)
+    q.push(0, 0.5)
+    with pytest.raises(_lib.LtError):
+        q.push(2, 0.5)       # out of order
+    with pytest.raises(_lib.LtError):
+        q.push(1, math.inf)  # not finite
+    with pytest.raises(_lib.LtError):
+        api.LazyQueue(3, 4)
+
+
+def test_kv_bytes_matches_oracle(L):
+    from kv_cache_compression_causal_amd import api
+    for (B, Hkv, N, D, dt, S, R) in [(1, 8, 32768, 128, 1, 4, 1020), (8, 8, 100000, 128, 1, 4, 1020),
+                                     (2, 3, 10, 64, 0, 4, 20)]:
+        e = 2 if dt == 1 else 4
+        assert api.lt_kv_bytes(B, Hkv, N, D, dt, S, R) == oracle.kv_bytes(B, Hkv, N, D, e, S, R)

@@ -1,0 +1,157 @@
+"""GPU parity: every kernel through the C ABI against the fp64 oracle.
+
+Small shapes span several tiles and a ragged tail; GQA group sizes 1-8 cover
+every workgroup layout; edge cases: N = 1, W = N, S = 0, S + R >= N.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_causal_amd import ops, synth
+from helpers import (TOL_BF16_LSE, TOL_BF16_OUT, TOL_BF16_RATIO, TOL_F32, assert_close, np64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _tol(dtype):
+    if dtype == torch.float32:
+        return TOL_F32, TOL_F32, TOL_F32
+    return TOL_BF16_OUT, TOL_BF16_LSE, TOL_BF16_RATIO
+
+
+PREFILL_CASES = [
+    # B, N, Hq, Hkv, D, dtype, S, R, W, seed
+    (1, 512, 4, 1, 64, torch.float32, 4, 60, 32, 1),      # tiny workload shape
+    (1, 200, 8, 2, 128, torch.bfloat16, 4, 60, 32, 11),   # G=4, ragged
+    (2, 300, 10, 2, 128, torch.bfloat16, 4, 100, 40, 12), # G=5, B=2
+    (1, 333, 3, 3, 128, torch.bfloat16, 2, 50, 20, 13),   # G=1
+    (1, 257, 4, 2, 64, torch.bfloat16, 4, 33, 16, 14),    # G=2, D=64
+    (1, 190, 6, 2, 128, torch.bfloat16, 3, 70, 25, 15),   # G=3
+    (1, 150, 16, 2, 128, torch.bfloat16, 4, 40, 30, 16),  # G=8 (two chunks)
+    (1, 1, 5, 1, 128, torch.bfloat16, 4, 10, 1, 17),      # N=1
+    (1, 17, 5, 1, 128, torch.bfloat16, 0, 5, 17, 18),     # S=0, W=N
+    (1, 40, 5, 1, 128, torch.bfloat16, 8, 64, 10, 19),    # S+R >= N
+    (1, 300, 8, 2, 128, torch.float32, 4, 60, 50, 20),    # fp32 D=128 G=4
+    (2, 130, 6, 3, 64, torch.float32, 0, 7, 130, 21),     # fp32 W=N S=0
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,dtype,S,R,W,seed", PREFILL_CASES)
+def test_prefill_lse_lazy(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
+    print(f"prefill case B{B} N{N} Hq{Hq} Hkv{Hkv} D{D} {dtype} S{S} R{R} W{W}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, seed, dtype)
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, W=W)
+    out, lse, rows, ratio = ops.prefill(q.to(DEV), k.to(DEV), v.to(DEV), S, R, W)
+    torch.cuda.synchronize()
+    to, tl, tr = _tol(dtype)
+    assert_close("out", np64(out), ref["out"], to)
+    assert_close("lse", np64(lse), ref["lse"], tl)
+    assert_close("lazy_rows", np64(rows), ref["lazy_rows"], tr)
+    assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], tr)
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,dtype,S,R,W,seed", PREFILL_CASES)
+def test_prefill_plain_matches_lazy_variant(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
+    """W = 0 runs the kernel without the epilogue: out and lse are bit-identical."""
+    q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, seed, dtype))
+    out0, lse0, _, _ = ops.prefill(q, k, v, S, R, 0)
+    out1, lse1, _, _ = ops.prefill(q, k, v, S, R, W)
+    torch.cuda.synchronize()
+    assert torch.equal(out0, out1) and torch.equal(lse0, lse1)
+
+
+STREAM_CASES = [
+    (1, 512, 4, 1, 64, torch.float32, 4, 60, 1),
+    (1, 300, 8, 2, 128, torch.bfloat16, 4, 60, 2),
+    (2, 333, 10, 2, 128, torch.bfloat16, 4, 100, 3),
+    (1, 260, 3, 3, 128, torch.bfloat16, 0, 37, 4),
+    (1, 200, 4, 2, 64, torch.bfloat16, 70, 1, 5),      # R = 1: sinks + diagonal
+    (1, 100, 16, 2, 128, torch.bfloat16, 4, 200, 6),   # S + R >= N: full attention
+    (1, 257, 6, 2, 128, torch.float32, 3, 64, 7),
+]
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,dtype,S,R,seed", STREAM_CASES)
+def test_streaming(B, N, Hq, Hkv, D, dtype, S, R, seed):
+    print(f"streaming case B{B} N{N} Hq{Hq} Hkv{Hkv} D{D} {dtype} S{S} R{R}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, seed, dtype)
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, W=0, streaming=True, full=False)
+    out, lse = ops.streaming(q.to(DEV), k.to(DEV), v.to(DEV), S, R)
+    torch.cuda.synchronize()
+    to, tl, _ = _tol(dtype)
+    assert_close("sout", np64(out), ref["sout"], to)
+    assert_close("slse", np64(lse), ref["slse"], tl)
+
+
+DECODE_CASES = [
+    # B, Hq, Hkv, D, L, dtype, seed
+    (2, 10, 2, 128, 1, torch.bfloat16, 1),
+    (2, 10, 2, 128, 100, torch.bfloat16, 2),
+    (1, 40, 8, 128, 1024, torch.bfloat16, 3),
+    (3, 8, 2, 64, 5000, torch.bfloat16, 4),
+    (1, 16, 1, 128, 777, torch.bfloat16, 5),   # G = 16
+    (2, 4, 4, 128, 3000, torch.bfloat16, 6),   # G = 1
+    (2, 10, 2, 128, 700, torch.float32, 7),
+    (1, 4, 1, 64, 65, torch.float32, 8),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,L,dtype,seed", DECODE_CASES)
+def test_decode(B, Hq, Hkv, D, L, dtype, seed):
+    print(f"decode case B{B} Hq{Hq} Hkv{Hkv} D{D} L{L} {dtype}", flush=True)
+    q = synth.normal((B, Hq, D), seed, dtype)
+    k = synth.normal((B, Hkv, L, D), seed + 100, dtype)
+    v = synth.normal((B, Hkv, L, D), seed + 200, dtype)
+    ref = oracle.decode(np64(q), np64(k), np64(v))
+    out, lse = ops.decode(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    to, tl, _ = _tol(dtype)
+    assert_close("out", np64(out), ref["out"], to)
+    assert_close("lse", np64(lse), ref["lse"], tl)
+
+
+@pytest.mark.parametrize("N,S,R,dtype", [(300, 4, 60, torch.bfloat16), (50, 4, 60, torch.bfloat16),
+                                         (1000, 0, 100, torch.float32), (64, 64, 1, torch.bfloat16)])
+def test_compaction_bit_exact(N, S, R, dtype):
+    k = synth.normal((2, 3, N, 128), 31, dtype)
+    v = synth.normal((2, 3, N, 128), 32, dtype)
+    ks, vs = ops.compact(k.to(DEV), v.to(DEV), S, R)
+    torch.cuda.synchronize()
+    idx = oracle.streaming_rows(N, S, R)
+    assert torch.equal(ks.cpu(), k[:, :, idx, :])
+    assert torch.equal(vs.cpu(), v[:, :, idx, :])
+
+
+def test_lazy_ratio_equals_streaming_lse_gap():
+    """Per-row lazy ratio = exp(LSE_stream - LSE_full): two kernels, one identity."""
+    B, N, Hq, Hkv, D, S, R, W = 1, 700, 10, 2, 128, 4, 100, 64
+    q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, 41, torch.bfloat16))
+    _, lse, rows, _ = ops.prefill(q, k, v, S, R, W)
+    _, slse = ops.streaming(q, k, v, S, R)
+    torch.cuda.synchronize()
+    gap = torch.exp((slse[:, :, N - W:] - lse[:, :, N - W:]).double())
+    assert_close("ratio vs lse gap", np64(rows), gap.cpu().numpy(), 2e-3)
+
+
+def test_decode_on_compacted_cache_matches_streaming_last_row():
+    """Streaming decode over the compacted cache = streaming prefill at row N-1."""
+    B, N, Hq, Hkv, D, S, R = 2, 600, 10, 2, 128, 4, 100
+    q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, 42, torch.bfloat16))
+    sout, slse = ops.streaming(q, k, v, S, R)
+    ks, vs = ops.compact(k, v, S, R)
+    dout, dlse = ops.decode(q[:, :, N - 1, :].contiguous(), ks, vs)
+    torch.cuda.synchronize()
+    assert_close("out", np64(dout), np64(sout[:, :, N - 1, :]), 2e-2)
+    assert_close("lse", np64(dlse), np64(slse[:, :, N - 1]), 1e-3)
+
+
+def test_deterministic():
+    q, k, v = (t.to(DEV) for t in synth.qkv(1, 500, 10, 2, 128, 43, torch.bfloat16))
+    a = ops.prefill(q, k, v, 4, 60, 50)
+    b = ops.prefill(q, k, v, 4, 60, 50)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
