@@ -8,12 +8,14 @@
 // project page, "Introduction" -- converted layers run streaming attention.
 //
 // Work decomposition (one workgroup = 4 waves = 256 threads):
-//   a workgroup owns one (batch, KV head, chunk of GC query heads of that
-//   group) and BM = 64*PB consecutive query positions.  Wave w owns 16*PB of
-//   those positions for all GC heads: RB = GC*PB row blocks of 16 queries.
-//   Every K/V tile of BN keys is staged once in LDS and read by all four
-//   waves, so the GQA group shares each tile; inside a wave each K fragment
-//   read from LDS feeds RB matrix-core ops.
+//   the queries of one (batch, KV head) are flattened position-major over the
+//   G query heads of the group, r = position * G + head-in-group.  A
+//   workgroup owns 256 consecutive rows r, each wave 64 of them as RB = 4
+//   row blocks of 16.  Every K/V tile of BN keys is staged once in LDS and
+//   read by all four waves, so the whole GQA group shares each tile; inside
+//   a wave each K fragment read from LDS feeds RB matrix-core ops.  The
+//   causal mask uses each lane's own position, so rows of different heads
+//   and positions mix freely inside a row block.
 //
 // Matrix-core formulation (v_mfma_f32_16x16x32_bf16, 64 lanes, lane l:
 // c = l%16, g = l/16):
@@ -33,10 +35,14 @@
 //   reduced once at the end.  Scores are kept in log2 units (scale*log2 e
 //   folded into one fma before exp2).
 //
-// Launch order: blockIdx.x % U picks the (batch, KV head, chunk) unit so that
-// with B*Hkv*chunks a multiple of 8 each XCD (dispatch is round-robin over
-// the 8 XCDs) keeps one KV head's K/V in its own L2; blockIdx.x / U walks the
-// query tiles longest-first to even out the causal triangle.
+// Launch order: blockIdx.x % U picks the (batch, KV head) unit so that with
+// B*Hkv a multiple of 8 each XCD (dispatch is round-robin over the 8 XCDs)
+// keeps one KV head's K/V in its own L2; blockIdx.x / U walks the row tiles
+// longest-first to even out the causal triangle.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "lt_internal.h"
 
 namespace lt {
@@ -57,37 +63,83 @@ __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int D, int GC, int PB, int BN, int MODE>
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int RB = GC * PB;   // 16-query row blocks per wave
-    constexpr int BM = 64 * PB;   // query positions per workgroup
-    constexpr int KS = D / 32;    // 32-dim steps of Q.K
-    constexpr int DB = D / 16;    // 16-dim blocks of O
-    constexpr int NKB = BN / 16;  // 16-key blocks per tile
-    constexpr int NT2 = BN / 32;  // 32-key steps of P.V per tile
-    constexpr int STR = D + 16;   // LDS row stride (elements): rows shift by 32 B
-    constexpr int TILE = BN * STR;
-    constexpr int CH = BN * D / 8;  // 16-byte chunks per tile
-    static_assert(CH % 256 == 0, "tile must split evenly over 256 threads");
-    __shared__ __attribute__((aligned(16))) bf16 lds[2 * TILE];
-    bf16 *const Ks = lds;
-    bf16 *const Vs = lds + TILE;
+// LDS tiles are unpadded rows of D bf16, permuted in 16-byte chunks so that
+// the reads below are bank-conflict free: the 16 rows one 128-bit K read
+// touches, and the four 32-byte row pieces of each transposing V read, land
+// in distinct bank groups.  XOR makes each map its own inverse.
+template <int D>
+__device__ __forceinline__ int swz_k(int row, int chunk) {
+    return D == 128 ? chunk ^ (row & 15) : chunk ^ ((row >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int swz_v(int row, int chunk) {
+    return D == 128 ? chunk ^ (2 * (row & 7)) : chunk ^ (2 * ((row >> 1) & 3));
+}
+
+// Work decomposition: the queries of one (batch, KV head) are flattened
+// position-major over the G query heads of the group, r = position * G +
+// head-in-group.  A workgroup of NW = 8 waves (two per SIMD) owns NW*16*RB
+// consecutive rows r; each wave owns RB row blocks of 16.  K/V tiles of BT
+// keys are staged in LDS once per workgroup and read by every wave, so the
+// whole GQA group shares each tile; inside a wave each K fragment read from
+// LDS feeds RB matrix-core ops.  The causal mask uses each lane's own
+// position, so rows of different heads and positions mix freely inside a
+// row block.  While one wave of a SIMD runs its softmax or waits on LDS, the
+// other wave's matrix-core products run.
+//
+// The lazy-ratio numerator is accumulated in the same pass: on the key tiles
+// that hold sink or recent keys of an observed row (the last W queries), the
+// weights of the keys in that row's sink + recent set are summed next to the
+// full sum l, with the same running max and the same rescaling, so
+// r_i = lz_i / l_i = exp(ln lz_i + m_i - LSE_i) uses the LSE's own
+// denominator and costs O(S+R) extra work per observed query; no key tile is
+// read a second time.
+template <int D, int RB, int BT, int MODE>
+__global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
+    constexpr int NW = 8;            // waves per workgroup
+    constexpr int WROWS = 16 * RB;   // flattened query rows per wave
+    constexpr int BROWS = NW * WROWS;
+    constexpr int KS = D / 32;       // 32-dim steps of Q.K
+    constexpr int DB = D / 16;       // 16-dim blocks of O
+    constexpr int BN = 32;           // keys per softmax step (half a tile at BT = 64)
+    constexpr int NH = BT / BN;      // softmax steps per LDS tile
+    constexpr int NKB = BN / 16;     // 16-key blocks per step
+    constexpr int CPR = D / 8;       // 16-byte chunks per LDS row
+    constexpr int RPI = 64 / CPR;    // rows one wave fills per direct load
+    constexpr int NINST = BT / RPI;  // direct loads per tile (over all waves)
+    constexpr int NI = (NINST + NW - 1) / NW;
+    constexpr int TILE = BT * D;
+    static_assert(BT % RPI == 0, "tile rows must fill whole direct loads");
+    constexpr bool LAZY = MODE == MODE_FULL_LAZY;
+    __shared__ __attribute__((aligned(16))) bf16 lds[4 * TILE];  // K0 K1 V0 V1
+    bf16 *const Kbuf = lds;
+    bf16 *const Vbuf = lds + 2 * TILE;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 4, c16 = lane & 15;
-    const int U = a.B * a.Hkv * a.n_chunks;
+    const int U = a.B * a.Hkv;
     const int unit = (int)(blockIdx.x % U);
     const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / U);
-    const int chunk = unit % a.n_chunks;
-    const int bhk = unit / a.n_chunks;
-    const int hk = bhk % a.Hkv, b = bhk / a.Hkv;
-    const int N = a.N;
-    const int q0 = qt * BM;
-    const int wpos0 = q0 + wave * 16 * PB;
-    const int h0 = hk * a.G + chunk * GC;
+    const int hk = unit % a.Hkv, b = unit / a.Hkv;
+    const int N = a.N, G = a.G;
     const float c = a.c;
+    const int r0 = qt * BROWS;
+    const int rw0 = r0 + wave * WROWS;
+    const int nrows = N * G;
+    const int wg_last = ((r0 + BROWS < nrows ? r0 + BROWS : nrows) - 1) / G;  // last position
+    const int wg_first = r0 / G;
+    const int w_first = rw0 / G;               // first position of this wave
+    const int w_last = (rw0 + WROWS - 1) / G;  // last position of this wave
 
+    int pos[RB];   // query position of this lane's column in each row block
+    int head[RB];  // its query head
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        const int r = rw0 + rb * 16 + c16;
+        pos[rb] = r / G;
+        head[rb] = hk * G + (r - pos[rb] * G);
+    }
     const bf16 *kbase = (const bf16 *)a.k + b * a.k_sb + hk * a.k_sh;
     const bf16 *vbase = (const bf16 *)a.v + b * a.v_sb + hk * a.v_sh;
 
@@ -95,177 +147,205 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
     bf16x8 qreg[RB][KS];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        const int pos = wpos0 + (rb % PB) * 16 + c16;
-        const bf16 *qp = (const bf16 *)a.q + b * a.q_sb + (int64_t)(h0 + rb / PB) * a.q_sh +
-                         (int64_t)(pos < N ? pos : 0) * a.q_sn + g * 8;
+        const bool ok = pos[rb] < N;
+        const bf16 *qp = (const bf16 *)a.q + b * a.q_sb + (int64_t)(ok ? head[rb] : 0) * a.q_sh +
+                         (int64_t)(ok ? pos[rb] : 0) * a.q_sn + g * 8;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             bf16x8 v = *(const bf16x8 *)(qp + ks * 32);
-            if (pos >= N) v = bf16x8{};
-            qreg[rb][ks] = v;
+            qreg[rb][ks] = ok ? v : bf16x8{};
         }
     }
 
-    // Stage keys [t*BN, t*BN+BN) of K (and V) into LDS; rows past N are zero.
-    auto load_tile = [&](int t, bool with_v) {
-        const int key0 = t * BN;
+    // Direct global -> LDS loads (global_load_lds_dwordx4): lane i of a wave
+    // writes 16 bytes at dst + 16 i, so each lane fetches the global chunk
+    // that belongs at its swizzled LDS slot.  Rows past N are read from row
+    // N-1: their keys are never visible and their values meet zero weights.
+    auto load_tile = [&](const bf16 *src, int64_t sn, int t, bf16 *dst_tile, bool is_k) {
+        const int key0 = t * BT;
 #pragma unroll
-        for (int it = 0; it < CH / 256; ++it) {
-            const int cidx = it * 256 + tid;
-            const int r = cidx / (D / 8), c8 = cidx % (D / 8);
-            const int key = key0 + r;
-            bf16x8 kv = bf16x8{}, vv = bf16x8{};
-            if (key < N) {
-                kv = *(const bf16x8 *)(kbase + (int64_t)key * a.k_sn + c8 * 8);
-                if (with_v) vv = *(const bf16x8 *)(vbase + (int64_t)key * a.v_sn + c8 * 8);
-            }
-            *(bf16x8 *)(Ks + r * STR + c8 * 8) = kv;
-            if (with_v) *(bf16x8 *)(Vs + r * STR + c8 * 8) = vv;
+        for (int j = 0; j < NI; ++j) {
+            if (NINST % NW != 0 && wave + NW * j >= NINST) break;
+            const int row0 = RPI * (wave + NW * j);
+            const int row = row0 + lane / CPR, ph = lane % CPR;
+            const int key = key0 + row < N ? key0 + row : N - 1;
+            const int lch = is_k ? swz_k<D>(row, ph) : swz_v<D>(row, ph);
+            const bf16 *gp = src + (int64_t)key * sn + lch * 8;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
+                                             (__attribute__((address_space(3))) void *)(dst_tile + row0 * D),
+                                             16, 0, 0);
         }
     };
+    // Every wave's direct loads have landed and are visible to the workgroup.
+    auto loads_done = [&]() {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    };
 
-    // S^T for the staged tile: s[kb][rb] holds keys kb*16+4g+r, query column c16.
-    auto qk = [&](f32x4 (&s)[NKB][RB]) {
+    // S^T for keys [32h, 32h+32) of a staged tile: s[kb][rb] holds keys
+    // kb*16+4g+r of the step, query column c16.
+    auto qk = [&](const bf16 *Kb, int h, f32x4 (&s)[NKB][RB]) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
-                const bf16x8 A = *(const bf16x8 *)(Ks + (kb * 16 + c16) * STR + ks * 32 + g * 8);
+                const int row = BN * h + kb * 16 + c16;
+                const bf16x8 A = *(const bf16x8 *)(Kb + row * D + swz_k<D>(row, ks * 4 + g) * 8);
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
                     s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qreg[rb][ks],
                                                                         s[kb][rb], 0, 0, 0);
             }
+    };
+    // O^T += V^T P^T for keys [32h, 32h+32) of a staged V tile.
+    auto pv = [&](const bf16 *Vb, int h, const bf16x8 (&pk)[RB], f32x4 (&o)[RB][DB]) {
+        const int row1 = BN * h + 4 * g + (c16 >> 2), row2 = row1 + 16;
+        const int half = (c16 & 1) * 4;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            const int lch = 2 * db + ((c16 & 3) >> 1);
+            const bf16x8 A = concat(lds_read_tr(Vb + row1 * D + swz_v<D>(row1, lch) * 8 + half),
+                                    lds_read_tr(Vb + row2 * D + swz_v<D>(row2, lch) * 8 + half));
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pk[rb], o[rb][db], 0, 0, 0);
         }
     };
-
-    // Visible-key test of the attention variant.  Written with non-short-
-    // circuit & and | so that masking stays a per-lane select: the
-    // short-circuit form became exec-mask branches around the accumulator
-    // registers, and the compiler dropped one of those branches' writes.
+    // Visible-key test of the attention variant and the sink + recent set.
+    // Written with non-short-circuit & and | so that masking stays a per-lane
+    // select: the short-circuit form became exec-mask branches around the
+    // accumulator registers, and the compiler dropped one of those branches'
+    // writes.
+    auto in_set = [&](int j, int i) -> bool { return (j <= i) & ((j < a.S) | (j > i - a.R)); };
     auto visible = [&](int j, int i) -> bool {
-        if (MODE == MODE_STREAM) return (j <= i) & ((j < a.S) | (j > i - a.R));
+        if (MODE == MODE_STREAM) return in_set(j, i);
         return j <= i;
     };
 
     // Key tiles to visit: full attention sees tiles 0..nt-1; streaming sees
-    // the sink tiles and the band (q0-R, last query] of this workgroup.
-    const int last_row = (q0 + BM < N ? q0 + BM : N) - 1;
-    const int nt = last_row / BN + 1;
-    const int ns = a.S > 0 ? ((a.S - 1) / BN + 1 < nt ? (a.S - 1) / BN + 1 : nt) : 0;
-    int band0 = q0 - a.R + 1;
-    band0 = band0 < 0 ? 0 : band0 / BN;
+    // the sink tiles and the band (first position - R, last position].
+    const int nt = wg_last / BT + 1;
+    const int ns = a.S > 0 ? ((a.S - 1) / BT + 1 < nt ? (a.S - 1) / BT + 1 : nt) : 0;
+    int band0 = wg_first - a.R + 1;
+    band0 = band0 < 0 ? 0 : band0 / BT;
     if (band0 < ns) band0 = ns;
-    const int n_iter_sparse = ns + (nt - band0);
-    auto sparse_tile = [&](int it) { return it < ns ? it : band0 + (it - ns); };
+    const int n_iter = (MODE == MODE_STREAM) ? ns + (nt - band0) : nt;
+    auto tile_of = [&](int it) {
+        if (MODE == MODE_STREAM) return it < ns ? it : band0 + (it - ns);
+        return it;
+    };
+    // Observed rows of this wave (lazy ratio): positions >= N - W.
+    const int obs_lo = (w_first > N - a.W ? w_first : N - a.W);
+    const bool wave_obs = LAZY && w_last >= N - a.W;
 
     f32x4 o[RB][DB];
-    float m[RB], l[RB];
+    float m[RB], l[RB], lz[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         m[rb] = kNegInf;
         l[rb] = 0.f;
+        lz[rb] = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    const int n_iter = (MODE == MODE_STREAM) ? n_iter_sparse : nt;
-    const int wlast = wpos0 + 16 * PB - 1;  // last query position of this wave
+    load_tile(kbase, a.k_sn, tile_of(0), Kbuf, true);
+    load_tile(vbase, a.v_sn, tile_of(0), Vbuf, false);
+    loads_done();
     for (int it = 0; it < n_iter; ++it) {
-        const int t = (MODE == MODE_STREAM) ? sparse_tile(it) : it;
-        const int key0 = t * BN;
-        __syncthreads();
-        load_tile(t, true);
-        __syncthreads();
-        if (key0 > wlast) continue;  // every key of the tile is in this wave's future
-
-        f32x4 s[NKB][RB];
-        qk(s);
-
-        const bool need_mask = (MODE == MODE_STREAM) || (key0 + BN - 1 > wpos0);
-        if (need_mask) {
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = key0 + kb * 16 + 4 * g + r;
-                        const int i = wpos0 + (rb % PB) * 16 + c16;
-                        s[kb][rb][r] = visible(j, i) ? s[kb][rb][r] : kNegInf;
-                    }
+        const int buf = it & 1;
+        if (it + 1 < n_iter) {
+            load_tile(kbase, a.k_sn, tile_of(it + 1), Kbuf + (buf ^ 1) * TILE, true);
+            load_tile(vbase, a.v_sn, tile_of(it + 1), Vbuf + (buf ^ 1) * TILE, false);
         }
-
-        // Online softmax (log2 units) and P^T packing.
-        bf16x8 pk[NT2][RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float mx = kNegInf;
+        for (int h = 0; h < NH; ++h) {
+            const int key0 = tile_of(it) * BT + BN * h;
+            if (key0 > w_last) continue;  // every key of the step is in this wave's future
+            f32x4 s[NKB][RB];
+            qk(Kbuf + buf * TILE, h, s);
+            if ((MODE == MODE_STREAM) || (key0 + BN - 1 > w_first)) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m[rb], mx * c);
-            const float mref = (mnew == kNegInf) ? 0.f : mnew;
-            const float alpha = exp2_fast(m[rb] - mref);
-            m[rb] = mnew;
-            float rs = 0.f;
+                    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = key0 + kb * 16 + 4 * g + r;
+                            s[kb][rb][r] = visible(j, pos[rb]) ? s[kb][rb][r] : kNegInf;
+                        }
+            }
+            // Online softmax in log2 units.  The reference max of a row block
+            // only moves when some row's max grew by more than 8 (a factor
+            // 256): until then the weights stay below 2^8 and O, l, lz keep
+            // their scale, which skips almost all O rescaling.
+            bf16x8 pk[RB];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = exp2_fast(__builtin_fmaf(s[kb][rb][r], c, -mref));
-                    s[kb][rb][r] = p;
-                    rs += p;
+            for (int rb = 0; rb < RB; ++rb) {
+                float mx = kNegInf;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                const float mnew = fmaxf(m[rb], mx * c);
+                if (__any(mnew > m[rb] + 8.f)) {
+                    const float mref_new = (mnew == kNegInf) ? 0.f : mnew;
+                    const float alpha = exp2_fast(m[rb] - mref_new);
+                    m[rb] = mnew;
+                    l[rb] *= alpha;
+                    if (LAZY) lz[rb] *= alpha;
+#pragma unroll
+                    for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
                 }
-            l[rb] = l[rb] * alpha + rs;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
-#pragma unroll
-            for (int t2 = 0; t2 < NT2; ++t2) {
+                const float mref = (m[rb] == kNegInf) ? 0.f : m[rb];
+                float rs = 0.f;
                 bf16x8 p8;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    p8[e] = (bf16)s[2 * t2][rb][e];
-                    p8[e + 4] = (bf16)s[2 * t2 + 1][rb][e];
+                    const float p0 = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -mref));
+                    const float p1 = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -mref));
+                    s[0][rb][e] = p0;
+                    s[1][rb][e] = p1;
+                    rs += p0 + p1;
+                    p8[e] = (bf16)p0;
+                    p8[e + 4] = (bf16)p1;
                 }
-                pk[t2][rb] = p8;
+                pk[rb] = p8;
+                l[rb] += rs;
             }
-        }
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int t2 = 0; t2 < NT2; ++t2) {
-            const bf16 *vrow = Vs + (32 * t2 + 4 * g + (c16 >> 2)) * STR + 4 * (c16 & 3);
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const bf16x8 A = concat(lds_read_tr(vrow + db * 16), lds_read_tr(vrow + 16 * STR + db * 16));
+            // Lazy-ratio numerator on steps holding sink or recent keys of an
+            // observed row of this wave.
+            if (wave_obs && ((key0 < a.S) | (key0 + BN - 1 > obs_lo - a.R))) {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pk[t2][rb], o[rb][db],
-                                                                        0, 0, 0);
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const int j = key0 + kb * 16 + 4 * g + r;
+                            lz[rb] += in_set(j, pos[rb]) ? s[kb][rb][r] : 0.f;
+                        }
             }
+            pv(Vbuf + buf * TILE, h, pk, o);
         }
+        loads_done();
     }
 
-    // Finalize: O / l, LSE = (m + log2 l) * ln 2.
-    float lse2[RB];
+    // Finalize: O / l, LSE = (m + log2 l) * ln 2, lazy row = lz / l.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         float lt = l[rb] + __shfl_xor(l[rb], 16);
         lt += __shfl_xor(lt, 32);
         const float inv = 1.f / lt;
-        lse2[rb] = m[rb] + __log2f(lt);
-        const int pos = wpos0 + (rb % PB) * 16 + c16;
-        const int h = h0 + rb / PB;
-        if (pos < N) {
-            bf16 *op = (bf16 *)a.o + b * a.o_sb + (int64_t)h * a.o_sh + (int64_t)pos * a.o_sn + 4 * g;
+        if (pos[rb] < N) {
+            bf16 *op = (bf16 *)a.o + b * a.o_sb + (int64_t)head[rb] * a.o_sh +
+                       (int64_t)pos[rb] * a.o_sn + 4 * g;
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
                 bf16x4 w;
@@ -274,48 +354,13 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs a) {
                 *(bf16x4 *)(op + db * 16) = w;
             }
             if (a.lse != nullptr && g == 0)
-                a.lse[((int64_t)b * a.Hq + h) * N + pos] = lse2[rb] * kLn2;
+                a.lse[((int64_t)b * a.Hq + head[rb]) * N + pos[rb]] = (m[rb] + __log2f(lt)) * kLn2;
         }
-    }
-
-    // Lazy-ratio epilogue: only workgroups holding some of the last W queries.
-    // Numerator: recompute s_ij over the sink and recent key tiles only and
-    // sum exp2(s_ij*c - lse2_i) over j < S or i-R < j <= i; the denominator
-    // is the LSE just produced.
-    if (MODE == MODE_FULL_LAZY && q0 + BM > N - a.W) {
-        float acc[RB];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb] = 0.f;
-        for (int it = 0; it < n_iter_sparse; ++it) {
-            const int t = sparse_tile(it);
-            const int key0 = t * BN;
-            __syncthreads();
-            load_tile(t, false);
-            __syncthreads();
-            if (wlast < N - a.W || key0 > wlast) continue;
-            f32x4 s[NKB][RB];
-            qk(s);
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int j = key0 + kb * 16 + 4 * g + r;
-                        const int i = wpos0 + (rb % PB) * 16 + c16;
-                        const bool in_set = (j <= i) & ((j < a.S) | (j > i - a.R));
-                        const float e = exp2_fast(__builtin_fmaf(s[kb][rb][r], c, -lse2[rb]));
-                        acc[rb] += in_set ? e : 0.f;
-                    }
-        }
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-            float tot = acc[rb] + __shfl_xor(acc[rb], 16);
-            tot += __shfl_xor(tot, 32);
-            const int pos = wpos0 + (rb % PB) * 16 + c16;
-            const int h = h0 + rb / PB;
-            if (g == 0 && pos < N && pos >= N - a.W)
-                a.lazy_rows[((int64_t)b * a.Hq + h) * a.W + (pos - (N - a.W))] = tot;
+        if (LAZY) {
+            float zt = lz[rb] + __shfl_xor(lz[rb], 16);
+            zt += __shfl_xor(zt, 32);
+            if (g == 0 && pos[rb] < N && pos[rb] >= N - a.W)
+                a.lazy_rows[((int64_t)b * a.Hq + head[rb]) * a.W + (pos[rb] - (N - a.W))] = zt * inv;
         }
     }
 }
@@ -330,19 +375,23 @@ __global__ void lazy_reduce_kernel(const float *rows, float *ratio, int BH, int 
     ratio[i] = acc / (float)W;
 }
 
-template <int D, int GC, int PB, int BN>
-hipError_t launch_mode(const AttnArgs &a, int mode, hipStream_t st) {
-    dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv * a.n_chunks));
-    dim3 block(256);
+template <int D, int RB, int BT>
+hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
+    const int64_t rows = (int64_t)a.N * a.G;
+    const int brows = 8 * 16 * RB;
+    a.n_chunks = 1;
+    a.n_qtiles = (int)((rows + brows - 1) / brows);
+    dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv));
+    dim3 block(512);
     switch (mode) {
     case MODE_FULL:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, GC, PB, BN, MODE_FULL>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL>), grid, block, 0, st, a);
         break;
     case MODE_FULL_LAZY:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, GC, PB, BN, MODE_FULL_LAZY>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL_LAZY>), grid, block, 0, st, a);
         break;
     default:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, GC, PB, BN, MODE_STREAM>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_STREAM>), grid, block, 0, st, a);
         break;
     }
     return hipGetLastError();
@@ -350,26 +399,17 @@ hipError_t launch_mode(const AttnArgs &a, int mode, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
-    // Heads of a GQA group per workgroup (GC) and position blocks per wave
-    // (PB): up to 5 heads share each K/V tile; small groups take more
-    // positions per wave so each wave still owns 4-5 row blocks.
-    int gc = 1;
-    for (int cand = 5; cand >= 1; --cand)
-        if (a.G % cand == 0) { gc = cand; break; }
-    a.n_chunks = a.G / gc;
-    const int pb = gc == 1 ? 4 : gc == 2 ? 2 : 1;
-    const int bm = 64 * pb;
-    a.n_qtiles = (a.N + bm - 1) / bm;
-    // Key tile: 64 keys at D = 64; 32 at D = 128 so that O (RB*D/16 x 4),
-    // S^T (RB*BN/16 x 4) and Q^T (RB*D/16 x 2) fit the 512-register budget.
-    constexpr int BN = D == 64 ? 64 : 32;
-    switch (gc) {
-    case 1: return launch_mode<D, 1, 4, BN>(a, mode, st);
-    case 2: return launch_mode<D, 2, 2, BN>(a, mode, st);
-    case 3: return launch_mode<D, 3, 1, BN>(a, mode, st);
-    case 4: return launch_mode<D, 4, 1, BN>(a, mode, st);
-    default: return launch_mode<D, 5, 1, BN>(a, mode, st);
-    }
+    // Variant (LT_ATTN_VARIANT, for tuning): 1 = 3 row blocks per wave with
+    // 64-key tiles (default), 2 = 3 row blocks with 32-key tiles, 3 = 2 row
+    // blocks with 64-key tiles.  O (RB*D/16 x 4), S^T (RB x 8), Q^T
+    // (RB*D/16 x 2) and the rest must fit 256 registers for two waves per SIMD.
+    static int variant = [] {
+        const char *e = getenv("LT_ATTN_VARIANT");
+        return e ? atoi(e) : 1;
+    }();
+    if (variant == 2) return launch_cfg<D, 3, 32>(a, mode, st);
+    if (variant == 3) return launch_cfg<D, 2, 64>(a, mode, st);
+    return launch_cfg<D, 3, 64>(a, mode, st);
 }
 
 }  // namespace
