@@ -1,21 +1,12 @@
 // bf16 causal GQA attention on the gfx950 matrix cores: full prefill with LSE,
-// the fused lazy-ratio epilogue, and streaming (sink + recent) attention.
+// the lazy ratio computed in the same pass, and streaming (sink + recent)
+// attention.
 //
 // Method (LightTransfer pages): Chinese write-up, "solution 1" -- the LSE that
 // Flash Attention produces is the lazy ratio's denominator, the numerator
 // only needs the sink and recent keys; press-release page, "LightTransfer
 // method" -- the ratio is the attention mass on the initial and recent keys;
 // project page, "Introduction" -- converted layers run streaming attention.
-//
-// Work decomposition (one workgroup = 4 waves = 256 threads):
-//   the queries of one (batch, KV head) are flattened position-major over the
-//   G query heads of the group, r = position * G + head-in-group.  A
-//   workgroup owns 256 consecutive rows r, each wave 64 of them as RB = 4
-//   row blocks of 16.  Every K/V tile of BN keys is staged once in LDS and
-//   read by all four waves, so the whole GQA group shares each tile; inside
-//   a wave each K fragment read from LDS feeds RB matrix-core ops.  The
-//   causal mask uses each lane's own position, so rows of different heads
-//   and positions mix freely inside a row block.
 //
 // Matrix-core formulation (v_mfma_f32_16x16x32_bf16, 64 lanes, lane l:
 // c = l%16, g = l/16):
@@ -30,18 +21,15 @@
 //                   loads.  Both operands enumerate the 32 keys of a step in
 //                   the same (g, element) order, which is all the product
 //                   needs.
-//   Row statistics: max over a lane's own 4*BN/16 values, then across the
-//   four lane groups (xor 16, xor 32); the running sum stays per lane and is
-//   reduced once at the end.  Scores are kept in log2 units (scale*log2 e
-//   folded into one fma before exp2).
+//   Row statistics: max over a lane's own 8 values of a 32-key step, then
+//   across the four lane groups (permlane swaps, xor 16 and xor 32); the
+//   running sum stays per lane and is reduced once at the end.  Scores are
+//   kept in log2 units (scale*log2 e folded into one fma before exp2).
 //
 // Launch order: blockIdx.x % U picks the (batch, KV head) unit so that with
 // B*Hkv a multiple of 8 each XCD (dispatch is round-robin over the 8 XCDs)
 // keeps one KV head's K/V in its own L2; blockIdx.x / U walks the row tiles
 // longest-first to even out the causal triangle.
-#include <stdlib.h>
-
-#include <type_traits>
 
 #include "lt_internal.h"
 
@@ -58,6 +46,44 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
         (__attribute__((address_space(3))) i16x4 *)(p));
     return __builtin_bit_cast(bf16x4, r);
 }
+
+// Reductions across the four 16-lane groups holding one query column.
+// v_permlane16_swap / v_permlane32_swap exchange halves of two registers;
+// swapping a value with a copy of itself leaves, in each lane, its own
+// value and the value of lane l^16 (resp. l^32), in an order that depends
+// on the lane -- max and + do not care.  The swap is written in asm with
+// both registers as read-write operands: through the compiler builtin the
+// second result was dropped and the first read twice.  The s_nop on each
+// side gives the VALU -> permlane -> VALU wait states.
+__device__ __forceinline__ void permlane16_swap(unsigned &a, unsigned &b) {
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane32_swap(unsigned &a, unsigned &b) {
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    permlane16_swap(a, b);
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    permlane32_swap(a, b);
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    permlane16_swap(a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    unsigned a = __builtin_bit_cast(unsigned, x), b = a;
+    permlane32_swap(a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+// The row max / sum of a query column over the four lane groups.
+__device__ __forceinline__ float group_max(float x) { return max_xor32(max_xor16(x)); }
+__device__ __forceinline__ float group_sum(float x) { return sum_xor32(sum_xor16(x)); }
 
 __device__ __forceinline__ bf16x8 concat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -291,8 +317,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                mx = group_max(mx);
                 const float mnew = fmaxf(m[rb], mx * c);
                 if (__any(mnew > m[rb] + 8.f)) {
                     const float mref_new = (mnew == kNegInf) ? 0.f : mnew;
@@ -340,8 +365,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     // Finalize: O / l, LSE = (m + log2 l) * ln 2, lazy row = lz / l.
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        float lt = l[rb] + __shfl_xor(l[rb], 16);
-        lt += __shfl_xor(lt, 32);
+        const float lt = group_sum(l[rb]);
         const float inv = 1.f / lt;
         if (pos[rb] < N) {
             bf16 *op = (bf16 *)a.o + b * a.o_sb + (int64_t)head[rb] * a.o_sh +
@@ -357,8 +381,7 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
                 a.lse[((int64_t)b * a.Hq + head[rb]) * N + pos[rb]] = (m[rb] + __log2f(lt)) * kLn2;
         }
         if (LAZY) {
-            float zt = lz[rb] + __shfl_xor(lz[rb], 16);
-            zt += __shfl_xor(zt, 32);
+            const float zt = group_sum(lz[rb]);
             if (g == 0 && pos[rb] < N && pos[rb] >= N - a.W)
                 a.lazy_rows[((int64_t)b * a.Hq + head[rb]) * a.W + (pos[rb] - (N - a.W))] = zt * inv;
         }
@@ -399,16 +422,8 @@ hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
 
 template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
-    // Variant (LT_ATTN_VARIANT, for tuning): 1 = 3 row blocks per wave with
-    // 64-key tiles (default), 2 = 3 row blocks with 32-key tiles, 3 = 2 row
-    // blocks with 64-key tiles.  O (RB*D/16 x 4), S^T (RB x 8), Q^T
-    // (RB*D/16 x 2) and the rest must fit 256 registers for two waves per SIMD.
-    static int variant = [] {
-        const char *e = getenv("LT_ATTN_VARIANT");
-        return e ? atoi(e) : 1;
-    }();
-    if (variant == 2) return launch_cfg<D, 3, 32>(a, mode, st);
-    if (variant == 3) return launch_cfg<D, 2, 64>(a, mode, st);
+    // 3 row blocks per wave and 64-key tiles: O (3*D/16 x 4), S^T (3 x 8),
+    // Q^T (3*D/16 x 2) and the rest fit 256 registers for two waves per SIMD.
     return launch_cfg<D, 3, 64>(a, mode, st);
 }
 
