@@ -16,6 +16,8 @@
 //   tile through ds_read_b64_tr_b16.  Each 64-key tile is loaded with
 //   coalesced 128-bit global loads into LDS; wave w handles 16 of its keys.
 // fp32 path (vector ALUs): lane = pair of head dims, one key at a time.
+#include <type_traits>
+
 #include "lt_internal.h"
 
 namespace lt {
@@ -23,9 +25,7 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kTile = 64;  // keys per workgroup iteration (bf16 path)
-
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4_t;
+constexpr int kTile = 64;  // split granularity in keys
 
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -33,20 +33,54 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// V tiles in LDS use the same 16-byte-chunk swizzle as the prefill kernel,
+// so the transposing reads of a 32-key step are bank-conflict free.
+__device__ __forceinline__ int swz_v128(int row, int chunk) { return chunk ^ (2 * (row & 7)); }
+__device__ __forceinline__ int swz_v64(int row, int chunk) { return chunk ^ (2 * ((row >> 1) & 3)); }
+
+// Max over the four 16-lane groups of a column: v_permlane16/32_swap of a
+// value with a copy of itself leaves each lane its own value and that of
+// lane l^16 (l^32).  Issued in asm with both registers read-write (through
+// the compiler builtin one result was dropped); s_nop gives the wait states.
+__device__ __forceinline__ float group_max(float x) {
+    unsigned a0 = __builtin_bit_cast(unsigned, x), b0 = a0;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a0), "+v"(b0));
+    const float y = fmaxf(__builtin_bit_cast(float, a0), __builtin_bit_cast(float, b0));
+    unsigned a1 = __builtin_bit_cast(unsigned, y), b1 = a1;
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a1), "+v"(b1));
+    return fmaxf(__builtin_bit_cast(float, a1), __builtin_bit_cast(float, b1));
+}
+
+// s_waitcnt with only vmcnt limited (gfx9 encoding; expcnt/lgkmcnt left open).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // Partial state layout: ws[(bh * n_splits + split) * (D + 2) + {0..D-1: o/l, D: m (log2), D+1: l}]
+//
+// Each wave streams its own 32-key steps of the split (steps w, w+4, ...):
+// K goes straight from global memory into the matrix-core A operand (lane
+// (c, g) holds dims (D/4)g .. (D/4)(g+1)-1 of key c of a 16-key block,
+// contiguous bytes), one step ahead in registers; V goes by direct global->LDS loads
+// into a two-step ring private to the wave, read back transposed.  No
+// workgroup barrier until the four waves merge their states at the end.
 template <int D>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
-    constexpr int KS = D / 32;
-    constexpr int DB = D / 16;
-    constexpr int STR = D + 16;
-    constexpr int CH = kTile * D / 8;
-    // The K/V tiles and, after the key loop, the cross-wave merge buffer share LDS.
-    constexpr int TILE_BYTES = 2 * kTile * STR * (int)sizeof(bf16);
+    constexpr int KS = D / 32;       // 32-dim steps (Q.K)
+    constexpr int DB = D / 16;       // 16-dim blocks (O)
+    constexpr int STEP = 32;         // keys per step
+    constexpr int CPR = D / 8;       // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;    // rows per direct load
+    constexpr int NVL = STEP / RPI;  // direct loads per V step
+    constexpr int VTILE = STEP * D;  // elements per V step
+    constexpr int KPL = D / 32;      // 16-byte K loads per lane and 16-key block (D/4 dims)
+    // V rings (4 waves x 2 steps) and, after the key loop, the merge buffer.
+    constexpr int RING_BYTES = 4 * 2 * VTILE * (int)sizeof(bf16);
     constexpr int RED_BYTES = 4 * 16 * (D + 1) * (int)sizeof(float);
-    __shared__ __attribute__((aligned(16))) char smem[TILE_BYTES > RED_BYTES ? TILE_BYTES : RED_BYTES];
+    __shared__ __attribute__((aligned(16))) char smem[RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES];
     __shared__ float red_m[4][16], red_l[4][16];
-    bf16 *const Ks = (bf16 *)smem;
-    bf16 *const Vs = Ks + kTile * STR;
     float (*const red_o)[16][D + 1] = (float (*)[16][D + 1])smem;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -57,83 +91,123 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const int G = a.G;
     const int64_t kbeg = (int64_t)split * a.keys_per_split;
     const int64_t kend = kbeg + a.keys_per_split < a.kv_len ? kbeg + a.keys_per_split : a.kv_len;
+    const int nsteps = (int)((kend - kbeg + STEP - 1) / STEP);
     const float c = a.c;
+    bf16 *const ring = (bf16 *)smem + wave * 2 * VTILE;
 
     const bf16 *kbase = (const bf16 *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
     const bf16 *vbase = (const bf16 *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
 
+    // Q^T: lane holds column c16 (query head hk*G + c16, zero if c16 >= G),
+    // dims (D/4)g + 8ks .. +7 of step ks -- the same dim order as the K operand.
     bf16x8 qreg[KS];
     {
         const bool col_ok = c16 < G;
-        const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + (col_ok ? c16 : 0)) * D + g * 8;
+        const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + (col_ok ? c16 : 0)) * D + (D / 4) * g;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 v = *(const bf16x8 *)(qp + ks * 32);
-            if (!col_ok) v = bf16x8{};
-            qreg[ks] = v;
+            bf16x8 v = *(const bf16x8 *)(qp + 8 * ks);
+            qreg[ks] = col_ok ? v : bf16x8{};
         }
     }
+
+    bf16x8 kreg[2][2][KPL];  // [buffer][16-key block][load]
+    auto issue = [&](int t, int buf) {
+        const int64_t key0 = kbeg + (int64_t)t * STEP;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            int64_t key = key0 + kb * 16 + c16;
+            key = key < kend ? key : kend - 1;
+            const bf16 *kp = kbase + key * a.k_sn + (D / 4) * g;
+#pragma unroll
+            for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
+        }
+        bf16 *dst = ring + buf * VTILE;
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            const int row0 = RPI * u;
+            const int row = row0 + lane / CPR, ph = lane % CPR;
+            int64_t key = key0 + row;
+            key = key < kend ? key : kend - 1;
+            const int lch = D == 128 ? swz_v128(row, ph) : swz_v64(row, ph);
+            const bf16 *gp = vbase + key * a.v_sn + lch * 8;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
+                                             (__attribute__((address_space(3))) void *)(dst + row0 * D),
+                                             16, 0, 0);
+        }
+    };
 
     f32x4 o[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m = kNegInf, l = 0.f;
 
-    for (int64_t t0 = kbeg; t0 < kend; t0 += kTile) {
-        __syncthreads();
+    // One step of this wave: t is the step, BUF (compile time, so the K
+    // registers stay registers) the buffer holding it.
+    auto step = [&](int t, auto buf_c) {
+        constexpr int BUF = decltype(buf_c)::value;
+        const bool next = t + 4 < nsteps;
+        if (next) issue(t + 4, BUF ^ 1);
+        // This step's K registers and V tile have landed once at most the
+        // next step's loads are outstanding.
+        if (next) wait_vmcnt<2 * KPL + NVL>();
+        else wait_vmcnt<0>();
+        const int64_t key0 = kbeg + (int64_t)t * STEP;
+
+        f32x4 s[2];
 #pragma unroll
-        for (int it = 0; it < CH / 256; ++it) {
-            const int cidx = it * 256 + tid;
-            const int r = cidx / (D / 8), c8 = cidx % (D / 8);
-            const int64_t key = t0 + r;
-            bf16x8 kv = bf16x8{}, vv = bf16x8{};
-            if (key < kend) {
-                kv = *(const bf16x8 *)(kbase + key * a.k_sn + c8 * 8);
-                vv = *(const bf16x8 *)(vbase + key * a.v_sn + c8 * 8);
-            }
-            *(bf16x8 *)(Ks + r * STR + c8 * 8) = kv;
-            *(bf16x8 *)(Vs + r * STR + c8 * 8) = vv;
-        }
-        __syncthreads();
-        const int64_t wkey0 = t0 + 16 * wave;
-        if (wkey0 >= kend) continue;
-        f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kb = 0; kb < 2; ++kb) {
+            s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 A = *(const bf16x8 *)(Ks + (16 * wave + c16) * STR + ks * 32 + g * 8);
-            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qreg[ks], s, 0, 0, 0);
+            for (int ks = 0; ks < KS; ++ks)
+                s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kreg[BUF][kb][ks], qreg[ks], s[kb], 0, 0, 0);
         }
         float mx = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (wkey0 + 4 * g + r >= kend) s[r] = kNegInf;
-            mx = fmaxf(mx, s[r]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                s[kb][r] = key0 + kb * 16 + 4 * g + r < kend ? s[kb][r] : kNegInf;
+                mx = fmaxf(mx, s[kb][r]);
+            }
+        mx = group_max(mx);
         const float mnew = fmaxf(m, mx * c);
         const float alpha = __builtin_amdgcn_exp2f(m - mnew);
         m = mnew;
-        bf16x4 p4;
+        bf16x8 p8;
         float rs = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c, -mnew));
-            rs += p;
-            p4[r] = (bf16)p;
+        for (int e = 0; e < 4; ++e) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[0][e], c, -mnew));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[1][e], c, -mnew));
+            rs += p0 + p1;
+            p8[e] = (bf16)p0;
+            p8[e + 4] = (bf16)p1;
         }
         l = l * alpha + rs;
-        const bf16 *vrow = Vs + (16 * wave + 4 * g + (c16 >> 2)) * STR + 4 * (c16 & 3);
+        const bf16 *Vb = ring + BUF * VTILE;
+        const int row1 = 4 * g + (c16 >> 2), row2 = row1 + 16;
+        const int half = (c16 & 1) * 4;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
+            const int lch = 2 * db + ((c16 & 3) >> 1);
+            const int p1 = D == 128 ? swz_v128(row1, lch) : swz_v64(row1, lch);
+            const int p2 = D == 128 ? swz_v128(row2, lch) : swz_v64(row2, lch);
+            const bf16x8 A = __builtin_shufflevector(lds_read_tr(Vb + row1 * D + p1 * 8 + half),
+                                                     lds_read_tr(Vb + row2 * D + p2 * 8 + half),
+                                                     0, 1, 2, 3, 4, 5, 6, 7);
             o[db] *= alpha;
-            const bf16x4 A = lds_read_tr(vrow + db * 16);
-            o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, p4, o[db], 0, 0, 0);
+            o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, p8, o[db], 0, 0, 0);
         }
+    };
+    if (wave < nsteps) issue(wave, 0);
+    for (int t = wave; t < nsteps; t += 8) {
+        step(t, std::integral_constant<int, 0>{});
+        if (t + 4 < nsteps) step(t + 4, std::integral_constant<int, 1>{});
     }
 
     // Merge the four waves' states for each column, then store the split's partial.
-    __syncthreads();  // every wave is done reading the K/V tiles
+    __syncthreads();  // every wave is done with its V ring
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if (g == 0) {
@@ -231,10 +305,11 @@ __global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
 }  // namespace
 
 int decode_num_splits(int B, int Hkv, int64_t kv_len) {
-    // Aim for about 1024 workgroups (4 per CU) so that enough 64-key tiles are
-    // in flight to cover HBM latency; never fewer than one tile per split.
+    // Aim for about 512 workgroups (two per CU, eight waves streaming their
+    // own steps) so enough loads are in flight to cover HBM latency; never
+    // fewer than one 64-key chunk per split.
     const int64_t units = (int64_t)B * Hkv;
-    int64_t want = (1024 + units - 1) / units;
+    int64_t want = (512 + units - 1) / units;
     const int64_t max_splits = (kv_len + kTile - 1) / kTile;
     if (want > max_splits) want = max_splits;
     if (want < 1) want = 1;
