@@ -1,6 +1,6 @@
 """Benchmark of the LightTransfer-Test hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-driver] [--no-cpu]
 
 Headline leg (the step): one LightTransfer-Test layer at the qwen32k shape
 (B1 N32768 Hq40 Hkv8 D128 bf16, keys of tokens 0..3 x3, S4 R1020 W128):
@@ -9,11 +9,12 @@ ratios to the host, layer score into the lazy-layer queue, and the KV of the
 evicted layer compacted to its sink + recent slice.  value = algorithmic
 prefill + lazy-numerator FLOP per step / wall time per step.
 
-Other legs, reported beside it: the same prefill without the epilogue
-(lazy-ratio overhead), streaming attention on the same tensors, and one
-hybrid decode step at B8 / 100000-token context over 64 layers (32 full,
-32 streaming at 1024 rows; one distinct buffer per layer; the 64 calls are
-captured once in a HIP graph and replayed).
+Other legs, reported beside it: the same prefill without the lazy ratio
+(its overhead), streaming attention on the same tensors, one hybrid decode
+step at B8 / 100000-token context over 64 layers (32 full, 32 streaming at
+1024 rows; one distinct buffer per layer; the 64 calls are captured once in
+a HIP graph and replayed), and the 64-layer LightTransfer-Test prefill
+(selected layers, eviction order, KV bytes).
 
 roofline: the prefill+lazy kernel, FLOP per launch over its mean duration
 from HIP events on the launch stream, against the 2.5 PFLOP/s dense bf16
@@ -78,6 +79,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-driver", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=98304,
                     help="rows of the oracle's CPU sample")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
@@ -270,6 +272,36 @@ def main() -> int:
                             "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
                             "bytes_per_step": bytes_step}
         del graph, qs, ks_, vs_, outs, lses, ws
+        torch.cuda.empty_cache()
+
+    # The 64-layer LightTransfer-Test prefill: selection and KV bytes
+    if not args.no_driver:
+        from kv_cache_compression_causal_amd import driver
+        dw = synth.DRIVER64
+        log("running the 64-layer driver")
+
+        def layer_inputs(l):
+            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=dev)
+            return ql, kl, vl
+
+        res = driver.run(layer_inputs, int(dw.extra["layers"]), int(dw.extra["capacity"]), dw.S, dw.R,
+                         dw.W, timing=True)
+        srt = sorted(res.layer_score)
+        MiB = 1 << 20
+        L64 = res.layers
+        result["driver64"] = {
+            "workload": "driver64: 64 layers of the qwen32k shape, per-layer sink scale and recency "
+                        "bias, queue capacity 32, S4 R1020 W128",
+            "streaming_layers": [l for l in range(L64) if res.is_streaming[l]],
+            "evicted_at_step": res.evicted_at_step,
+            "kv_all_full_MiB": L64 * res.full_bytes / MiB,
+            "kv_retained_final_MiB": res.retained_bytes[-1] / MiB,
+            "kv_peak_transient_MiB": max(res.transient_bytes) / MiB,
+            "min_adjacent_score_gap": min(b - a for a, b in zip(srt, srt[1:])),
+            "prefill_ms_mean": round(sum(res.prefill_ms) / len(res.prefill_ms), 4),
+        }
+        log(f"driver64: retained {res.retained_bytes[-1] / MiB:.0f} MiB of {L64 * res.full_bytes / MiB:.0f}, "
+            f"peak {max(res.transient_bytes) / MiB:.0f} MiB")
         torch.cuda.empty_cache()
 
     # CPU baseline: the oracle on a bounded row sample of the same workload

@@ -162,6 +162,16 @@ int lt_lazy_queue_push(lt_lazy_queue *queue, int layer, double score, int *evict
 void lt_lazy_queue_destroy(lt_lazy_queue *queue);
 
 /*
+ * Same push, with the layer's score computed here from its n per-(batch,
+ * head) lazy ratios (head_ratio, host fp32, e.g. the lazy_ratio output of
+ * lt_prefill_attn_lse_lazy copied to the host): their mean, summed in fp64
+ * in index order.  *score (may be NULL) receives it.  Non-finite ratios
+ * give LT_ERR_VALUE and leave the queue unchanged.
+ */
+int lt_lazy_queue_push_ratios(lt_lazy_queue *queue, int layer, const float *head_ratio, int n,
+                              double *score, int *evicted);
+
+/*
  * Batch form of the same queue.  head_ratio [L][n] host fp32: the n
  * per-(batch, head) lazy ratios of each layer.  A layer's score is their
  * mean, summed in fp64 in index order (written to layer_score [L] if not

@@ -18,7 +18,7 @@ LT_F32, LT_BF16 = 0, 1
 EXPORTS = (
     "lt_prefill_attn_lse_lazy", "lt_streaming_attn", "lt_hybrid_decode_workspace_bytes",
     "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
-    "lt_lazy_queue_push", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
+    "lt_lazy_queue_push", "lt_lazy_queue_push_ratios", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
     "lt_last_error",
 )
 
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.lt_lazy_queue_create.restype = c_int
     L.lt_lazy_queue_push.argtypes = [c_void_p, c_int, ctypes.c_double, ctypes.POINTER(c_int)]
     L.lt_lazy_queue_push.restype = c_int
+    L.lt_lazy_queue_push_ratios.argtypes = [c_void_p, c_int, fp, c_int, ctypes.POINTER(ctypes.c_double),
+                                            ctypes.POINTER(c_int)]
+    L.lt_lazy_queue_push_ratios.restype = c_int
     L.lt_lazy_queue_destroy.argtypes = [c_void_p]
     L.lt_lazy_queue_destroy.restype = None
     L.lt_select_lazy_layers.argtypes = [fp, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_double),

@@ -147,6 +147,17 @@ class LazyQueue:
         check(lib().lt_lazy_queue_push(self._h, layer, float(score), ctypes.byref(ev)))
         return ev.value
 
+    def push_ratios(self, layer: int, head_ratio) -> Tuple[int, float]:
+        """Push with the score computed in the library from the layer's
+        per-(batch, head) ratios (host, fp32).  Returns (evicted, score)."""
+        hr = np.ascontiguousarray(np.asarray(head_ratio, dtype=np.float32).reshape(-1))
+        ev = ctypes.c_int()
+        sc = ctypes.c_double()
+        check(lib().lt_lazy_queue_push_ratios(self._h, layer,
+                                              hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+                                              hr.size, ctypes.byref(sc), ctypes.byref(ev)))
+        return ev.value, sc.value
+
     def close(self) -> None:
         if self._h:
             lib().lt_lazy_queue_destroy(self._h)

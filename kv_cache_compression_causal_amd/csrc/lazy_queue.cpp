@@ -69,6 +69,18 @@ struct lt_lazy_queue {
 namespace {
 // Shares the thread-local error text of lt_api.cpp through a tiny setter.
 int qfail(int code, const char *msg);
+
+// A layer's score: the mean of its n ratios, summed in fp64 in index order.
+// Returns false if a ratio is not finite.
+bool mean_of(const float *x, int n, double *out) {
+    double acc = 0.0;
+    for (int i = 0; i < n; ++i) {
+        if (isnan(x[i]) || isinf(x[i])) return false;
+        acc += (double)x[i];
+    }
+    *out = acc / (double)n;
+    return true;
+}
 }  // namespace
 
 extern "C" {
@@ -98,6 +110,18 @@ int lt_lazy_queue_push(lt_lazy_queue *q, int layer, double score, int *evicted) 
 
 void lt_lazy_queue_destroy(lt_lazy_queue *q) { delete q; }
 
+int lt_lazy_queue_push_ratios(lt_lazy_queue *q, int layer, const float *head_ratio, int n,
+                              double *score, int *evicted) {
+    if (q == nullptr || head_ratio == nullptr || evicted == nullptr)
+        return qfail(LT_ERR_NULL, "queue/head_ratio/evicted is NULL");
+    if (n < 1) return qfail(LT_ERR_SHAPE, "n must be >= 1");
+    double sc;
+    if (!mean_of(head_ratio, n, &sc)) return qfail(LT_ERR_VALUE, "head ratio is not finite");
+    const int e = lt_lazy_queue_push(q, layer, sc, evicted);
+    if (e == LT_OK && score != nullptr) *score = sc;
+    return e;
+}
+
 int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
                           int *evicted_at_step, uint8_t *is_streaming) {
     if (head_ratio == nullptr || evicted_at_step == nullptr || is_streaming == nullptr)
@@ -105,15 +129,9 @@ int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *
     if (L < 1 || n < 1) return qfail(LT_ERR_SHAPE, "L and n must be >= 1");
     if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
     std::vector<double> score((size_t)L);
-    for (int l = 0; l < L; ++l) {
-        double acc = 0.0;
-        for (int i = 0; i < n; ++i) {
-            const float x = head_ratio[(size_t)l * n + i];
-            if (isnan(x) || isinf(x)) return qfail(LT_ERR_VALUE, "head ratio is not finite");
-            acc += (double)x;
-        }
-        score[l] = acc / (double)n;
-    }
+    for (int l = 0; l < L; ++l)
+        if (!mean_of(head_ratio + (size_t)l * n, n, &score[l]))
+            return qfail(LT_ERR_VALUE, "head ratio is not finite");
     lt_lazy_queue q;
     q.L = L; q.C = C; q.next = 0;
     q.heap.reserve((size_t)C + 1);

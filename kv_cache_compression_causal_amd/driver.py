@@ -1,0 +1,142 @@
+"""LightTransfer-Test prefill over a stack of layers, through the C ABI.
+
+For each layer in order (LightTransfer project page, Figure 2 caption;
+Chinese write-up, "solution 2"):
+  1. causal GQA prefill with LSE and the per-head lazy ratio (one call);
+  2. the per-head ratios go to the host; the layer score is their mean;
+  3. the score enters the lazy-layer queue; if the queue holds more than C
+     layers, the highest-score layer leaves and its KV cache is compacted to
+     the sink + recent rows and the full copy released.
+The KV bytes held after each step (and while a layer's full KV is added,
+before the queue's decision) are tracked, so the peak prefill KV can be
+checked against C full layers + the rest streaming.
+
+Run the 64-layer workload:  python -m kv_cache_compression_causal_amd.driver
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import sys
+import time
+from dataclasses import dataclass, field
+from typing import Callable, Dict, List, Optional, Tuple
+
+import torch
+
+from . import api, ops, synth
+from ._lib import LT_BF16, LT_F32
+
+
+@dataclass
+class DriverResult:
+    layers: int
+    capacity: int
+    head_ratio: List[List[float]]           # [L][B*Hq] lazy ratio per (batch, head)
+    layer_score: List[float]                # fp64 mean of each layer's ratios
+    evicted_at_step: List[int]              # layer evicted after layer l's push, or -1
+    is_streaming: List[int]                 # 1 for layers converted to streaming
+    retained_bytes: List[int]               # KV bytes held after step l
+    transient_bytes: List[int]              # KV bytes held at step l before the queue's pop
+    full_bytes: int
+    stream_bytes: int
+    prefill_ms: List[float] = field(default_factory=list)
+    wall_s: float = 0.0
+
+
+def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], layers: int,
+        capacity: int, S: int, R: int, W: int, timing: bool = False) -> DriverResult:
+    """Run the layer stack.  ``layer_inputs(l)`` returns (q, k, v) for layer l
+    on the device; the layer's k, v are its KV cache."""
+    queue = api.LazyQueue(layers, capacity)
+    kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
+    streaming_kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
+    head_ratio, scores, evicted, retained, transient, times = [], [], [], [], [], []
+    is_stream = [0] * layers
+    full_b = stream_b = 0
+    out = lse = rows = ratio = None
+    t_start = time.perf_counter()
+    for l in range(layers):
+        q, k, v = layer_inputs(l)
+        B, Hq, N, D = q.shape
+        Hkv = k.shape[1]
+        if out is None or out.shape != q.shape or out.dtype != q.dtype:
+            out = torch.empty_like(q)
+            lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+            rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+            ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+            dt = LT_BF16 if q.dtype == torch.bfloat16 else LT_F32
+            full_b, stream_b = api.lt_kv_bytes(B, Hkv, N, D, dt, S, R)
+        if timing:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+        api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
+        if timing:
+            e1.record()
+        r = ratio.reshape(-1).cpu().numpy()   # the per-layer device -> host sync
+        if timing:
+            times.append(e0.elapsed_time(e1))
+        kv[l] = (k, v)
+        del q
+        held = sum(stream_b if is_stream[x] else full_b for x in range(l)) + full_b
+        transient.append(held)
+        ev, score = queue.push_ratios(l, r)
+        if ev >= 0:
+            kf, vf = kv.pop(ev)
+            streaming_kv[ev] = ops.compact(kf, vf, S, R)
+            del kf, vf   # the full KV of the evicted layer is released
+            is_stream[ev] = 1
+        head_ratio.append([float(x) for x in r])
+        scores.append(score)
+        evicted.append(ev)
+        retained.append(sum(stream_b if is_stream[x] else full_b for x in range(l + 1)))
+    torch.cuda.synchronize()
+    queue.close()
+    return DriverResult(layers, capacity, head_ratio, scores, evicted, is_stream, retained, transient,
+                        full_b, stream_b, times, time.perf_counter() - t_start)
+
+
+def main(argv: Optional[List[str]] = None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--layers", type=int, default=None)
+    args = ap.parse_args(argv)
+    w = synth.DRIVER64
+    L = args.layers or int(w.extra["layers"])
+    C = int(w.extra["capacity"]) if args.layers is None else L // 2
+    dev = torch.device("cuda:0")
+
+    def inputs(l):
+        q, k, v, _, _ = synth.driver_layer(l, w, device=dev)
+        return q, k, v
+
+    print(f"[driver] {L} layers of B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D}, capacity {C}",
+          file=sys.stderr, flush=True)
+    res = run(inputs, L, C, w.S, w.R, w.W, timing=True)
+    srt = sorted(res.layer_score)
+    gaps = [b - a for a, b in zip(srt, srt[1:])]
+    MiB = 1 << 20
+    flop = 4.0 * w.B * w.Hq * w.D * w.N * (w.N + 1) / 2
+    report = {
+        "workload": f"driver64: {L} layers, B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D} bf16, "
+                    f"S{w.S} R{w.R} W{w.W}, capacity {C}",
+        "streaming_layers": [l for l in range(L) if res.is_streaming[l]],
+        "full_layers": [l for l in range(L) if not res.is_streaming[l]],
+        "evicted_at_step": res.evicted_at_step,
+        "layer_score": res.layer_score,
+        "score_min": min(res.layer_score), "score_max": max(res.layer_score),
+        "min_adjacent_score_gap": min(gaps) if gaps else None,
+        "kv_all_full_MiB": L * res.full_bytes / MiB,
+        "kv_retained_final_MiB": res.retained_bytes[-1] / MiB,
+        "kv_peak_transient_MiB": max(res.transient_bytes) / MiB,
+        "kv_reduction_pct": 100.0 * (1 - res.retained_bytes[-1] / (L * res.full_bytes)),
+        "prefill_ms_mean": sum(res.prefill_ms) / len(res.prefill_ms),
+        "prefill_tflops": flop / (sum(res.prefill_ms) / len(res.prefill_ms) * 1e-3) / 1e12,
+        "wall_s": res.wall_s,
+    }
+    print(json.dumps(report), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

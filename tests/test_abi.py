@@ -157,6 +157,10 @@ def test_select_matches_oracle_bit_exact(L, seed):
     q = api.LazyQueue(Lyr, C)
     assert [q.push(l, s) for l, s in enumerate(want_scores)] == wev
     q.close()
+    q = api.LazyQueue(Lyr, C)
+    pushed = [q.push_ratios(l, row) for l, row in enumerate(hr)]
+    assert [e for e, _ in pushed] == wev and [s for _, s in pushed] == want_scores
+    q.close()
 
 
 def test_queue_errors(L):

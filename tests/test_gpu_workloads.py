@@ -1,0 +1,108 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the
+bench times: outputs the oracle can afford are checked row by row (every
+head's last W rows, the first rows and seeded random rows), plus the
+multi-layer LightTransfer-Test driver end to end."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_causal_amd import driver, ops, synth
+from helpers import TOL_BF16_LSE, TOL_BF16_OUT, TOL_BF16_RATIO, assert_close, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _sample_rows(N, W, n_rand, seed):
+    rng = np.random.default_rng(seed)
+    rows = set(range(N - W, N)) | set(range(0, 64)) | set(int(x) for x in rng.integers(0, N, n_rand))
+    return np.array(sorted(rows), dtype=np.int32)
+
+
+def _check_prefill_workload(w, n_rand, heads=None):
+    print(f"workload {w.name}: generating on device", flush=True)
+    q, k, v = synth.workload_qkv(w, device=DEV)
+    out, lse, rows, ratio = ops.prefill(q, k, v, w.S, w.R, w.W)
+    sout, slse = ops.streaming(q, k, v, w.S, w.R)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    got_ratio = np64(ratio)
+    want_ratio = np.empty((w.B, w.Hq))
+    for b in range(w.B):
+        kh = {hk: (np64(k[b, hk]), np64(v[b, hk])) for hk in range(w.Hkv)}
+        for h in (range(w.Hq) if heads is None else heads):
+            pos = _sample_rows(w.N, w.W, n_rand, seed=1000 * b + h)
+            qr = np64(q[b, h][torch.as_tensor(pos, device=DEV, dtype=torch.long)])
+            r = oracle.rows(kh[h // G][0], kh[h // G][1], pos, qr, S=w.S, R=w.R)
+            pt = torch.as_tensor(pos, device=DEV, dtype=torch.long)
+            assert_close(f"out h{h}", np64(out[b, h][pt]), r["out"], TOL_BF16_OUT)
+            assert_close(f"lse h{h}", np64(lse[b, h][pt]), r["lse"], TOL_BF16_LSE)
+            assert_close(f"stream out h{h}", np64(sout[b, h][pt]), r["sout"], TOL_BF16_OUT)
+            assert_close(f"stream lse h{h}", np64(slse[b, h][pt]), r["slse"], TOL_BF16_LSE)
+            obs = pos >= w.N - w.W
+            assert_close(f"lazy rows h{h}", np64(rows[b, h])[pos[obs] - (w.N - w.W)], r["lazy"][obs],
+                         TOL_BF16_RATIO)
+            want_ratio[b, h] = r["lazy"][obs].sum() / w.W
+            assert abs(got_ratio[b, h] - want_ratio[b, h]) <= TOL_BF16_RATIO
+    return got_ratio
+
+
+def test_mistral8k_full_size():
+    _check_prefill_workload(synth.MISTRAL8K, n_rand=64)
+
+
+def test_qwen32k_full_size():
+    ratio = _check_prefill_workload(synth.QWEN32K, n_rand=32, heads=list(range(0, 40, 3)))
+    assert np.all((ratio >= 0) & (ratio <= 1))
+
+
+@pytest.mark.parametrize("layer", [0, 40])  # a full (100000-row) and a streaming (1024-row) layer
+def test_decode100k_full_size(layer):
+    w = synth.DECODE100K
+    q, k, v = synth.decode_layer(layer, w, device=DEV)
+    out, lse = ops.decode(q, k, v)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hk in [(0, 0), (w.B - 1, w.Hkv - 1), (3, 5)]:
+        r = oracle.decode(np64(q[b:b + 1, hk * G:(hk + 1) * G]), np64(k[b:b + 1, hk:hk + 1]),
+                          np64(v[b:b + 1, hk:hk + 1]))
+        assert_close(f"decode out b{b} hk{hk}", np64(out[b:b + 1, hk * G:(hk + 1) * G]), r["out"], TOL_BF16_OUT)
+        assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
+
+
+def test_driver_small_stack():
+    """8 layers with the driver's sink/recency recipe at N=1024: per-layer ratios
+    against the oracle, the queue bit for bit on the same fp32 ratios, the
+    end-to-end selection, and the KV accounting."""
+    w = synth.Workload("driver-small", 1, 1024, 10, 2, 128, torch.bfloat16, 4000, 4, 100, 32,
+                       extra={"layers": 8, "capacity": 4})
+    cache = {}
+
+    def inputs(l):
+        q, k, v, _, _ = synth.driver_layer(l, w, device=DEV, recent=w.R)
+        cache[l] = (np64(q), np64(k), np64(v))
+        return q, k, v
+
+    res = driver.run(inputs, 8, 4, w.S, w.R, w.W)
+    want_scores = []
+    for l in range(8):
+        qh, kh, vh = cache[l]
+        ref = oracle.prefill(qh, kh, vh, S=w.S, R=w.R, W=w.W, full=False)
+        np.testing.assert_allclose(np.array(res.head_ratio[l]), ref["lazy_ratio"].reshape(-1),
+                                   atol=TOL_BF16_RATIO)
+        want_scores.append(oracle.layer_score(ref["lazy_ratio"].reshape(-1)))
+    # (i) the same fp32 ratios through the oracle's queue: identical, bit for bit
+    gpu_scores = [oracle.layer_score(np.array(r, dtype=np.float32).astype(np.float64)) for r in res.head_ratio]
+    assert gpu_scores == res.layer_score
+    ev, st = oracle.select_lazy_layers(gpu_scores, 4)
+    assert ev == res.evicted_at_step and st == res.is_streaming
+    # (ii) end to end with the oracle's own ratios, when no two scores are within tolerance
+    srt = sorted(want_scores)
+    if min(b - a for a, b in zip(srt, srt[1:])) > 2 * TOL_BF16_RATIO:
+        ev2, _ = oracle.select_lazy_layers(want_scores, 4)
+        assert ev2 == res.evicted_at_step
+    acc = oracle.kv_accounting(res.evicted_at_step, res.full_bytes, res.stream_bytes)
+    assert acc["retained"] == res.retained_bytes and acc["transient"] == res.transient_bytes
+    full, stream = oracle.kv_bytes(1, 2, 1024, 128, 2, w.S, w.R)
+    assert (res.full_bytes, res.stream_bytes) == (full, stream)
