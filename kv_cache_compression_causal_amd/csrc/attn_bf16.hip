@@ -31,6 +31,8 @@
 // keeps one KV head's K/V in its own L2; blockIdx.x / U walks the row tiles
 // longest-first to even out the causal triangle.
 
+#include <type_traits>
+
 #include "lt_internal.h"
 
 namespace lt {
@@ -38,10 +40,13 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
+// Initial running max (log2 units): finite, so exp2(s - m) needs no -inf
+// guard, and far below any score, so the first visible key always resets it.
+constexpr float kMInit = -1e30f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *__restrict__ p) {
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4 *)(p));
     return __builtin_bit_cast(bf16x4, r);
@@ -120,9 +125,8 @@ __device__ __forceinline__ int swz_v(int row, int chunk) {
 // r_i = lz_i / l_i = exp(ln lz_i + m_i - LSE_i) uses the LSE's own
 // denominator and costs O(S+R) extra work per observed query; no key tile is
 // read a second time.
-template <int D, int RB, int BT, int MODE>
-__global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
-    constexpr int NW = 8;            // waves per workgroup
+template <int D, int RB, int BT, int MODE, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bf16_kernel(AttnArgs a) {
     constexpr int WROWS = 16 * RB;   // flattened query rows per wave
     constexpr int BROWS = NW * WROWS;
     constexpr int KS = D / 32;       // 32-dim steps of Q.K
@@ -138,11 +142,11 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     static_assert(BT % RPI == 0, "tile rows must fill whole direct loads");
     constexpr bool LAZY = MODE == MODE_FULL_LAZY;
     __shared__ __attribute__((aligned(16))) bf16 lds[4 * TILE];  // K0 K1 V0 V1
-    bf16 *const Kbuf = lds;
-    bf16 *const Vbuf = lds + 2 * TILE;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    // The wave index is uniform; readfirstlane lets the compiler see that, so
+    // every per-wave test below is a scalar branch, not an exec-mask one.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int U = a.B * a.Hkv;
     const int unit = (int)(blockIdx.x % U);
@@ -272,28 +276,30 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
     float m[RB], l[RB], lz[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-        m[rb] = kNegInf;
+        m[rb] = kMInit;
         l[rb] = 0.f;
         lz[rb] = 0.f;
 #pragma unroll
         for (int db = 0; db < DB; ++db) o[rb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    load_tile(kbase, a.k_sn, tile_of(0), Kbuf, true);
-    load_tile(vbase, a.v_sn, tile_of(0), Vbuf, false);
-    loads_done();
-    for (int it = 0; it < n_iter; ++it) {
-        const int buf = it & 1;
+    // One key tile: prefetch the next tile into the other buffer, then the
+    // tile's 32-key steps.  BUF is a compile-time constant so that every LDS
+    // address of the steps is a fixed offset.
+    auto run_tile = [&](int it, auto buf_c) {
+        constexpr int BUF = decltype(buf_c)::value;
+        bf16 *const Kb = lds + BUF * TILE;
+        bf16 *const Vb = lds + (2 + BUF) * TILE;
         if (it + 1 < n_iter) {
-            load_tile(kbase, a.k_sn, tile_of(it + 1), Kbuf + (buf ^ 1) * TILE, true);
-            load_tile(vbase, a.v_sn, tile_of(it + 1), Vbuf + (buf ^ 1) * TILE, false);
+            load_tile(kbase, a.k_sn, tile_of(it + 1), lds + (BUF ^ 1) * TILE, true);
+            load_tile(vbase, a.v_sn, tile_of(it + 1), lds + (2 + (BUF ^ 1)) * TILE, false);
         }
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             const int key0 = tile_of(it) * BT + BN * h;
             if (key0 > w_last) continue;  // every key of the step is in this wave's future
             f32x4 s[NKB][RB];
-            qk(Kbuf + buf * TILE, h, s);
+            qk(Kb, h, s);
             if ((MODE == MODE_STREAM) || (key0 + BN - 1 > w_first)) {
 #pragma unroll
                 for (int kb = 0; kb < NKB; ++kb)
@@ -305,10 +311,13 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
                             s[kb][rb][r] = visible(j, pos[rb]) ? s[kb][rb][r] : kNegInf;
                         }
             }
-            // Online softmax in log2 units.  The reference max of a row block
-            // only moves when some row's max grew by more than 8 (a factor
-            // 256): until then the weights stay below 2^8 and O, l, lz keep
-            // their scale, which skips almost all O rescaling.
+            // Online softmax in log2 units.  The reference max m of a row
+            // only moves when the row's max grew past m + 8 (a factor 256):
+            // until then the weights stay below 2^8 and O, l, lz keep their
+            // scale, which skips almost all O rescaling.  Whether any row of
+            // the block grew that much is known from each lane's own 8
+            // scores; only then is the row max taken across the four lane
+            // groups and the block rescaled.
             bf16x8 pk[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
@@ -317,27 +326,24 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
-                mx = group_max(mx);
-                const float mnew = fmaxf(m[rb], mx * c);
-                if (__any(mnew > m[rb] + 8.f)) {
-                    const float mref_new = (mnew == kNegInf) ? 0.f : mnew;
-                    const float alpha = exp2_fast(m[rb] - mref_new);
+                if (__any(mx * c > m[rb] + 8.f)) {
+                    const float mnew = fmaxf(m[rb], group_max(mx) * c);
+                    const float alpha = exp2_fast(m[rb] - mnew);
                     m[rb] = mnew;
                     l[rb] *= alpha;
                     if (LAZY) lz[rb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
                 }
-                const float mref = (m[rb] == kNegInf) ? 0.f : m[rb];
-                float rs = 0.f;
+                float rs;
                 bf16x8 p8;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -mref));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -mref));
+                    const float p0 = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
+                    const float p1 = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
                     s[0][rb][e] = p0;
                     s[1][rb][e] = p1;
-                    rs += p0 + p1;
+                    rs = e == 0 ? p0 + p1 : rs + (p0 + p1);
                     p8[e] = (bf16)p0;
                     p8[e + 4] = (bf16)p1;
                 }
@@ -357,10 +363,20 @@ __global__ __launch_bounds__(512) void attn_bf16_kernel(AttnArgs a) {
                             lz[rb] += in_set(j, pos[rb]) ? s[kb][rb][r] : 0.f;
                         }
             }
-            pv(Vbuf + buf * TILE, h, pk, o);
+            pv(Vb, h, pk, o);
         }
         loads_done();
+    };
+
+    load_tile(kbase, a.k_sn, tile_of(0), lds, true);
+    load_tile(vbase, a.v_sn, tile_of(0), lds + 2 * TILE, false);
+    loads_done();
+    int it = 0;
+    for (; it + 1 < n_iter; it += 2) {
+        run_tile(it, std::integral_constant<int, 0>{});
+        run_tile(it + 1, std::integral_constant<int, 1>{});
     }
+    if (it < n_iter) run_tile(it, std::integral_constant<int, 0>{});
 
     // Finalize: O / l, LSE = (m + log2 l) * ln 2, lazy row = lz / l.
 #pragma unroll
@@ -398,23 +414,23 @@ __global__ void lazy_reduce_kernel(const float *rows, float *ratio, int BH, int 
     ratio[i] = acc / (float)W;
 }
 
-template <int D, int RB, int BT>
+template <int D, int RB, int BT, int NW>
 hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     const int64_t rows = (int64_t)a.N * a.G;
-    const int brows = 8 * 16 * RB;
+    const int brows = NW * 16 * RB;
     a.n_chunks = 1;
     a.n_qtiles = (int)((rows + brows - 1) / brows);
     dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv));
-    dim3 block(512);
+    dim3 block(64 * NW);
     switch (mode) {
     case MODE_FULL:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL, NW>), grid, block, 0, st, a);
         break;
     case MODE_FULL_LAZY:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL_LAZY>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL_LAZY, NW>), grid, block, 0, st, a);
         break;
     default:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_STREAM>), grid, block, 0, st, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_STREAM, NW>), grid, block, 0, st, a);
         break;
     }
     return hipGetLastError();
@@ -424,7 +440,7 @@ template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
     // 3 row blocks per wave and 64-key tiles: O (3*D/16 x 4), S^T (3 x 8),
     // Q^T (3*D/16 x 2) and the rest fit 256 registers for two waves per SIMD.
-    return launch_cfg<D, 3, 64>(a, mode, st);
+    return launch_cfg<D, 3, 64, 8>(a, mode, st);
 }
 
 }  // namespace

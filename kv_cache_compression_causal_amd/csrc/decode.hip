@@ -8,13 +8,13 @@
 // from each K/V row, keeping one online-softmax state per head.  A second
 // kernel merges the per-split states with their log-sum-exps.
 //
-// bf16 path (matrix cores, v_mfma 16x16x32 for Q.K, 16x16x16 for P.V):
+// bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16 for Q.K and P.V):
 //   S^T (16 keys x 16 columns) = K Q^T, where column c < G is query head
 //   hk*G + c and the rest are zero padding; the column layout keeps each
 //   head's softmax state in the lanes that own its column.  O^T += V^T P^T
 //   takes P^T straight from the S^T registers and V^T from the row-major V
-//   tile through ds_read_b64_tr_b16.  Each 64-key tile is loaded with
-//   coalesced 128-bit global loads into LDS; wave w handles 16 of its keys.
+//   rows through ds_read_b64_tr_b16.  Each wave streams its own 32-key steps
+//   with coalesced 128-bit loads, one step ahead.
 // fp32 path (vector ALUs): lane = pair of head dims, one key at a time.
 #include <type_traits>
 
@@ -27,7 +27,7 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kTile = 64;  // split granularity in keys
 
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *p) {
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *__restrict__ p) {
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4 *)(p));
     return __builtin_bit_cast(bf16x4, r);
@@ -51,39 +51,38 @@ __device__ __forceinline__ float group_max(float x) {
     return fmaxf(__builtin_bit_cast(float, a1), __builtin_bit_cast(float, b1));
 }
 
-// s_waitcnt with only vmcnt limited (gfx9 encoding; expcnt/lgkmcnt left open).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Partial state layout: ws[(bh * n_splits + split) * (D + 2) + {0..D-1: o/l, D: m (log2), D+1: l}]
 //
 // Each wave streams its own 32-key steps of the split (steps w, w+4, ...):
 // K goes straight from global memory into the matrix-core A operand (lane
 // (c, g) holds dims (D/4)g .. (D/4)(g+1)-1 of key c of a 16-key block,
-// contiguous bytes), one step ahead in registers; V goes by direct global->LDS loads
-// into a two-step ring private to the wave, read back transposed.  No
-// workgroup barrier until the four waves merge their states at the end.
+// contiguous bytes), one step ahead in registers.  V rows are loaded one step
+// ahead into registers too (coalesced 128-bit loads), written at the start
+// of their step into an LDS slot private to the wave and read back
+// transposed.  All loads are plain register loads, so the compiler's
+// load-counter waits stay exact (mixing in direct global->LDS loads made it
+// wait for every outstanding load).  No workgroup barrier until the four
+// waves merge their states at the end.
 template <int D>
 __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;       // 32-dim steps (Q.K)
     constexpr int DB = D / 16;       // 16-dim blocks (O)
     constexpr int STEP = 32;         // keys per step
     constexpr int CPR = D / 8;       // 16-byte chunks per row
-    constexpr int RPI = 64 / CPR;    // rows per direct load
-    constexpr int NVL = STEP / RPI;  // direct loads per V step
+    constexpr int RPI = 64 / CPR;    // V rows per wave-wide 128-bit load
+    constexpr int NVL = STEP / RPI;  // V loads per lane and step
     constexpr int VTILE = STEP * D;  // elements per V step
     constexpr int KPL = D / 32;      // 16-byte K loads per lane and 16-key block (D/4 dims)
-    // V rings (4 waves x 2 steps) and, after the key loop, the merge buffer.
-    constexpr int RING_BYTES = 4 * 2 * VTILE * (int)sizeof(bf16);
+    // V slots (one step per wave) and, after the key loop, the merge buffer.
+    constexpr int RING_BYTES = 4 * VTILE * (int)sizeof(bf16);
     constexpr int RED_BYTES = 4 * 16 * (D + 1) * (int)sizeof(float);
     __shared__ __attribute__((aligned(16))) char smem[RING_BYTES > RED_BYTES ? RING_BYTES : RED_BYTES];
     __shared__ float red_m[4][16], red_l[4][16];
     float (*const red_o)[16][D + 1] = (float (*)[16][D + 1])smem;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // readfirstlane marks the wave index uniform, so the per-step tests are
+    // scalar branches and the load counters are tracked exactly across them.
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int split = blockIdx.x;
     const int bhk = blockIdx.y;
@@ -93,7 +92,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     const int64_t kend = kbeg + a.keys_per_split < a.kv_len ? kbeg + a.keys_per_split : a.kv_len;
     const int nsteps = (int)((kend - kbeg + STEP - 1) / STEP);
     const float c = a.c;
-    bf16 *const ring = (bf16 *)smem + wave * 2 * VTILE;
+    bf16 *const slot = (bf16 *)smem + wave * VTILE;
 
     const bf16 *kbase = (const bf16 *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
     const bf16 *vbase = (const bf16 *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
@@ -112,6 +111,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     }
 
     bf16x8 kreg[2][2][KPL];  // [buffer][16-key block][load]
+    bf16x8 vreg[NVL];        // V rows of the next step: row RPI*u + lane/CPR, chunk lane%CPR
     auto issue = [&](int t, int buf) {
         const int64_t key0 = kbeg + (int64_t)t * STEP;
 #pragma unroll
@@ -122,18 +122,21 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
             for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
         }
-        bf16 *dst = ring + buf * VTILE;
 #pragma unroll
         for (int u = 0; u < NVL; ++u) {
-            const int row0 = RPI * u;
-            const int row = row0 + lane / CPR, ph = lane % CPR;
-            int64_t key = key0 + row;
+            int64_t key = key0 + RPI * u + lane / CPR;
             key = key < kend ? key : kend - 1;
-            const int lch = D == 128 ? swz_v128(row, ph) : swz_v64(row, ph);
-            const bf16 *gp = vbase + key * a.v_sn + lch * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
-                                             (__attribute__((address_space(3))) void *)(dst + row0 * D),
-                                             16, 0, 0);
+            vreg[u] = *(const bf16x8 *)(vbase + key * a.v_sn + (lane % CPR) * 8);
+        }
+    };
+    // Write the staged V rows into the wave's slot, each 16-byte chunk at
+    // its swizzled place.
+    auto stage_v = [&]() {
+#pragma unroll
+        for (int u = 0; u < NVL; ++u) {
+            const int row = RPI * u + lane / CPR, ph = lane % CPR;
+            const int pc = D == 128 ? swz_v128(row, ph) : swz_v64(row, ph);
+            *(bf16x8 *)(slot + row * D + pc * 8) = vreg[u];
         }
     };
 
@@ -143,15 +146,17 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     float m = kNegInf, l = 0.f;
 
     // One step of this wave: t is the step, BUF (compile time, so the K
-    // registers stay registers) the buffer holding it.
-    auto step = [&](int t, auto buf_c) {
+    // registers stay registers) the buffer holding its K.  The step stages
+    // its V rows, then (with PREFETCH) issues the loads of step t + 4, whose
+    // latency the rest of the step covers.  The slot's previous contents
+    // were consumed by the last step's transposing reads, which completed
+    // before that step's products; LDS accesses of one wave run in order.
+    auto step = [&](int t, auto buf_c, auto prefetch_c) {
         constexpr int BUF = decltype(buf_c)::value;
-        const bool next = t + 4 < nsteps;
-        if (next) issue(t + 4, BUF ^ 1);
-        // This step's K registers and V tile have landed once at most the
-        // next step's loads are outstanding.
-        if (next) wait_vmcnt<2 * KPL + NVL>();
-        else wait_vmcnt<0>();
+        stage_v();
+        if constexpr (decltype(prefetch_c)::value) issue(t + 4, BUF ^ 1);
+        // Lanes read rows other lanes wrote: keep the reads below the writes.
+        asm volatile("" ::: "memory");
         const int64_t key0 = kbeg + (int64_t)t * STEP;
 
         f32x4 s[2];
@@ -185,7 +190,7 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             p8[e + 4] = (bf16)p1;
         }
         l = l * alpha + rs;
-        const bf16 *Vb = ring + BUF * VTILE;
+        const bf16 *Vb = slot;
         const int row1 = 4 * g + (c16 >> 2), row2 = row1 + 16;
         const int half = (c16 & 1) * 4;
 #pragma unroll
@@ -200,14 +205,29 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, p8, o[db], 0, 0, 0);
         }
     };
-    if (wave < nsteps) issue(wave, 0);
-    for (int t = wave; t < nsteps; t += 8) {
-        step(t, std::integral_constant<int, 0>{});
-        if (t + 4 < nsteps) step(t + 4, std::integral_constant<int, 1>{});
+    // The wave's steps are wave, wave + 4, ...; pairs whose successors all
+    // exist run without a branch between issue and wait, so the compiler's
+    // load-counter bookkeeping stays exact (a conditional prefetch made it
+    // fall back to waiting for every load at each step).
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+    using Pf = std::true_type;
+    using Last = std::false_type;
+    int t = wave;
+    if (t < nsteps) issue(t, 0);
+    for (; t + 8 < nsteps; t += 8) {
+        step(t, B0{}, Pf{});
+        step(t + 4, B1{}, Pf{});
+    }
+    if (t + 4 < nsteps) {
+        step(t, B0{}, Pf{});
+        step(t + 4, B1{}, Last{});
+    } else if (t < nsteps) {
+        step(t, B0{}, Last{});
     }
 
     // Merge the four waves' states for each column, then store the split's partial.
-    __syncthreads();  // every wave is done with its V ring
+    __syncthreads();  // every wave is done with its V slot
     float lt = l + __shfl_xor(l, 16);
     lt += __shfl_xor(lt, 32);
     if (g == 0) {
