@@ -311,22 +311,34 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                             s[kb][rb][r] = visible(j, pos[rb]) ? s[kb][rb][r] : kNegInf;
                         }
             }
-            // Online softmax in log2 units.  The reference max m of a row
-            // only moves when the row's max grew past m + 8 (a factor 256):
-            // until then the weights stay below 2^8 and O, l, lz keep their
-            // scale, which skips almost all O rescaling.  Whether any row of
-            // the block grew that much is known from each lane's own 8
-            // scores; only then is the row max taken across the four lane
-            // groups and the block rescaled.
+            // Online softmax in log2 units.  Weights are taken against the
+            // running reference max m of each row, which is allowed to lag the
+            // true max by up to a factor 2^8: a lane's 8 weights of the step
+            // sum to at most 256 while no row outgrew m by more than that, and
+            // O, l, lz then keep their scale.  Only when some lane's sum
+            // exceeds 256 (always on a row block's first visible keys, since m
+            // starts far below any score) is the row max taken across the four
+            // lane groups, the block rescaled and its weights recomputed.
             bf16x8 pk[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
-                float mx = kNegInf;
+                float p[NKB][4];
+                float rs;
+                auto weights = [&]() {
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+                    for (int e = 0; e < 4; ++e) {
+                        p[0][e] = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
+                        p[1][e] = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
+                        rs = e == 0 ? p[0][e] + p[1][e] : rs + (p[0][e] + p[1][e]);
+                    }
+                };
+                weights();
+                if (__any(rs > 256.f)) {
+                    float mx = kNegInf;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
-                if (__any(mx * c > m[rb] + 8.f)) {
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
                     const float mnew = fmaxf(m[rb], group_max(mx) * c);
                     const float alpha = exp2_fast(m[rb] - mnew);
                     m[rb] = mnew;
@@ -334,18 +346,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     if (LAZY) lz[rb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
+                    weights();
                 }
-                float rs;
                 bf16x8 p8;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const float p0 = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
-                    const float p1 = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
-                    s[0][rb][e] = p0;
-                    s[1][rb][e] = p1;
-                    rs = e == 0 ? p0 + p1 : rs + (p0 + p1);
-                    p8[e] = (bf16)p0;
-                    p8[e + 4] = (bf16)p1;
+                    s[0][rb][e] = p[0][e];
+                    s[1][rb][e] = p[1][e];
+                    p8[e] = (bf16)p[0][e];
+                    p8[e + 4] = (bf16)p[1][e];
                 }
                 pk[rb] = p8;
                 l[rb] += rs;
