@@ -189,21 +189,45 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // Direct global -> LDS loads (global_load_lds_dwordx4): lane i of a wave
     // writes 16 bytes at dst + 16 i, so each lane fetches the global chunk
-    // that belongs at its swizzled LDS slot.  Rows past N are read from row
-    // N-1: their keys are never visible and their values meet zero weights.
-    auto load_tile = [&](const bf16 *src, int64_t sn, int t, bf16 *dst_tile, bool is_k) {
-        const int key0 = t * BT;
+    // that belongs at its swizzled LDS slot.  The lane's byte offset within
+    // a tile is fixed; only the tile's base address (uniform) moves.  In a
+    // tile that runs past N, rows past N are read from row N-1: their keys
+    // are never visible and their values meet zero weights.
+    uint32_t koff[NI], voff[NI];
 #pragma unroll
-        for (int j = 0; j < NI; ++j) {
-            if (NINST % NW != 0 && wave + NW * j >= NINST) break;
-            const int row0 = RPI * (wave + NW * j);
-            const int row = row0 + lane / CPR, ph = lane % CPR;
-            const int key = key0 + row < N ? key0 + row : N - 1;
-            const int lch = is_k ? swz_k<D>(row, ph) : swz_v<D>(row, ph);
-            const bf16 *gp = src + (int64_t)key * sn + lch * 8;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)gp,
-                                             (__attribute__((address_space(3))) void *)(dst_tile + row0 * D),
-                                             16, 0, 0);
+    for (int j = 0; j < NI; ++j) {
+        const int row = RPI * (wave + NW * j) + lane / CPR, ph = lane % CPR;
+        koff[j] = (uint32_t)(((int64_t)row * a.k_sn + swz_k<D>(row, ph) * 8) * 2);
+        voff[j] = (uint32_t)(((int64_t)row * a.v_sn + swz_v<D>(row, ph) * 8) * 2);
+    }
+    auto load_tile = [&](int t, bf16 *Kd, bf16 *Vd) {
+        const int key0 = t * BT;
+        if (key0 + BT <= N) {
+            const char *kb = (const char *)(kbase + (int64_t)key0 * a.k_sn);
+            const char *vb = (const char *)(vbase + (int64_t)key0 * a.v_sn);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                if (NINST % NW != 0 && wave + NW * j >= NINST) break;
+                const int row0 = RPI * (wave + NW * j);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(kb + koff[j]),
+                                                 (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(vb + voff[j]),
+                                                 (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NI; ++j) {
+                if (NINST % NW != 0 && wave + NW * j >= NINST) break;
+                const int row0 = RPI * (wave + NW * j);
+                const int row = row0 + lane / CPR, ph = lane % CPR;
+                const int key = key0 + row < N ? key0 + row : N - 1;
+                const bf16 *kp = kbase + (int64_t)key * a.k_sn + swz_k<D>(row, ph) * 8;
+                const bf16 *vp = vbase + (int64_t)key * a.v_sn + swz_v<D>(row, ph) * 8;
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)kp,
+                                                 (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)vp,
+                                                 (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
+            }
         }
     };
     // Every wave's direct loads have landed and are visible to the workgroup.
@@ -290,10 +314,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         constexpr int BUF = decltype(buf_c)::value;
         bf16 *const Kb = lds + BUF * TILE;
         bf16 *const Vb = lds + (2 + BUF) * TILE;
-        if (it + 1 < n_iter) {
-            load_tile(kbase, a.k_sn, tile_of(it + 1), lds + (BUF ^ 1) * TILE, true);
-            load_tile(vbase, a.v_sn, tile_of(it + 1), lds + (2 + (BUF ^ 1)) * TILE, false);
-        }
+        if (it + 1 < n_iter) load_tile(tile_of(it + 1), lds + (BUF ^ 1) * TILE, lds + (2 + (BUF ^ 1)) * TILE);
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
             const int key0 = tile_of(it) * BT + BN * h;
@@ -319,21 +340,25 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             // exceeds 256 (always on a row block's first visible keys, since m
             // starts far below any score) is the row max taken across the four
             // lane groups, the block rescaled and its weights recomputed.
-            bf16x8 pk[RB];
+            __builtin_amdgcn_s_setprio(0);
+            float p[RB][NKB][4], rs[RB];
+            auto weights = [&]() {
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                float p[NKB][4];
-                float rs;
-                auto weights = [&]() {
+                for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        p[0][e] = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
-                        p[1][e] = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
-                        rs = e == 0 ? p[0][e] + p[1][e] : rs + (p[0][e] + p[1][e]);
+                        p[rb][0][e] = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
+                        p[rb][1][e] = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
+                        rs[rb] = e == 0 ? p[rb][0][e] + p[rb][1][e] : rs[rb] + (p[rb][0][e] + p[rb][1][e]);
                     }
-                };
-                weights();
-                if (__any(rs > 256.f)) {
+            };
+            weights();
+            bool outgrown = false;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) outgrown |= rs[rb] > 256.f;
+            if (__any(outgrown)) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
                     float mx = kNegInf;
 #pragma unroll
                     for (int kb = 0; kb < NKB; ++kb)
@@ -346,18 +371,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     if (LAZY) lz[rb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
-                    weights();
                 }
-                bf16x8 p8;
+                weights();
+            }
+            bf16x8 pk[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    s[0][rb][e] = p[0][e];
-                    s[1][rb][e] = p[1][e];
-                    p8[e] = (bf16)p[0][e];
-                    p8[e + 4] = (bf16)p[1][e];
+                    s[0][rb][e] = p[rb][0][e];
+                    s[1][rb][e] = p[rb][1][e];
+                    pk[rb][e] = (bf16)p[rb][0][e];
+                    pk[rb][e + 4] = (bf16)p[rb][1][e];
                 }
-                pk[rb] = p8;
-                l[rb] += rs;
+                l[rb] += rs[rb];
             }
             // Lazy-ratio numerator on steps holding sink or recent keys of an
             // observed row of this wave.
@@ -372,13 +399,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                             lz[rb] += in_set(j, pos[rb]) ? s[kb][rb][r] : 0.f;
                         }
             }
+            __builtin_amdgcn_s_setprio(1);
             pv(Vb, h, pk, o);
         }
         loads_done();
     };
 
-    load_tile(kbase, a.k_sn, tile_of(0), lds, true);
-    load_tile(vbase, a.v_sn, tile_of(0), lds + 2 * TILE, false);
+    load_tile(tile_of(0), lds, lds + 2 * TILE);
     loads_done();
     int it = 0;
     for (; it + 1 < n_iter; it += 2) {
