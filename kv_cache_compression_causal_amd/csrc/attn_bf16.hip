@@ -279,6 +279,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (MODE == MODE_STREAM) return in_set(j, i);
         return j <= i;
     };
+    // Scores of keys a row does not see become -inf.
+    auto mask = [&](f32x4 (&s)[NKB][RB], int key0) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int j = key0 + kb * 16 + 4 * g + r;
+                    s[kb][rb][r] = visible(j, pos[rb]) ? s[kb][rb][r] : kNegInf;
+                }
+    };
 
     // Key tiles to visit: full attention sees tiles 0..nt-1; streaming sees
     // the sink tiles and the band (first position - R, last position].
@@ -321,35 +333,39 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             if (key0 > w_last) continue;  // every key of the step is in this wave's future
             f32x4 s[NKB][RB];
             qk(Kb, h, s);
-            if ((MODE == MODE_STREAM) || (key0 + BN - 1 > w_first)) {
-#pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            const int j = key0 + kb * 16 + 4 * g + r;
-                            s[kb][rb][r] = visible(j, pos[rb]) ? s[kb][rb][r] : kNegInf;
-                        }
-            }
+            const bool masked = (MODE == MODE_STREAM) || (key0 + BN - 1 > w_first);
+            if (masked) mask(s, key0);
             // Online softmax in log2 units.  Weights are taken against the
             // running reference max m of each row, which is allowed to lag the
             // true max by up to a factor 2^8: a lane's 8 weights of the step
             // sum to at most 256 while no row outgrew m by more than that, and
             // O, l, lz then keep their scale.  Only when some lane's sum
             // exceeds 256 (always on a row block's first visible keys, since m
-            // starts far below any score) is the row max taken across the four
-            // lane groups, the block rescaled and its weights recomputed.
+            // starts far below any score) is the row max taken across the
+            // four lane groups, the block rescaled and the weights redone.
+            // Full attention writes the weights over the scores (registers
+            // are short) and on that rare path computes the step's scores
+            // again from the staged K tile; streaming attention, whose band
+            // rows take that path more often, keeps the scores instead.
             __builtin_amdgcn_s_setprio(0);
-            float p[RB][NKB][4], rs[RB];
+            constexpr bool INPLACE = MODE != MODE_STREAM;
+            float w[INPLACE ? 1 : RB][NKB][4];
+            float rs[RB];
             auto weights = [&]() {
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        p[rb][0][e] = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
-                        p[rb][1][e] = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
-                        rs[rb] = e == 0 ? p[rb][0][e] + p[rb][1][e] : rs[rb] + (p[rb][0][e] + p[rb][1][e]);
+                        const float p0 = exp2_fast(__builtin_fmaf(s[0][rb][e], c, -m[rb]));
+                        const float p1 = exp2_fast(__builtin_fmaf(s[1][rb][e], c, -m[rb]));
+                        if (INPLACE) {
+                            s[0][rb][e] = p0;
+                            s[1][rb][e] = p1;
+                        } else {
+                            w[INPLACE ? 0 : rb][0][e] = p0;
+                            w[INPLACE ? 0 : rb][1][e] = p1;
+                        }
+                        rs[rb] = e == 0 ? p0 + p1 : rs[rb] + (p0 + p1);
                     }
             };
             weights();
@@ -357,6 +373,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) outgrown |= rs[rb] > 256.f;
             if (__any(outgrown)) {
+                if (INPLACE) {
+                    qk(Kb, h, s);
+                    if (masked) mask(s, key0);
+                }
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) {
                     float mx = kNegInf;
@@ -374,15 +394,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 }
                 weights();
             }
+            if (!INPLACE) {
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        s[0][rb][e] = w[INPLACE ? 0 : rb][0][e];
+                        s[1][rb][e] = w[INPLACE ? 0 : rb][1][e];
+                    }
+            }
             bf16x8 pk[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    s[0][rb][e] = p[rb][0][e];
-                    s[1][rb][e] = p[rb][1][e];
-                    pk[rb][e] = (bf16)p[rb][0][e];
-                    pk[rb][e + 4] = (bf16)p[rb][1][e];
+                    pk[rb][e] = (bf16)s[0][rb][e];
+                    pk[rb][e + 4] = (bf16)s[1][rb][e];
                 }
                 l[rb] += rs[rb];
             }
