@@ -193,13 +193,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // a tile is fixed; only the tile's base address (uniform) moves.  In a
     // tile that runs past N, rows past N are read from row N-1: their keys
     // are never visible and their values meet zero weights.
-    uint32_t koff[NI], voff[NI];
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-        const int row = RPI * (wave + NW * j) + lane / CPR, ph = lane % CPR;
-        koff[j] = (uint32_t)(((int64_t)row * a.k_sn + swz_k<D>(row, ph) * 8) * 2);
-        voff[j] = (uint32_t)(((int64_t)row * a.v_sn + swz_v<D>(row, ph) * 8) * 2);
-    }
+    // A wave's loads of a tile cover rows RPI*(wave + NW j) + lane/CPR; the
+    // swizzle only depends on the row modulo 16, which is the same for every
+    // j, so load j of a lane sits a uniform RPI*NW rows after load 0.
+    const int row_l = RPI * wave + lane / CPR, ph_l = lane % CPR;
+    const uint32_t koff = (uint32_t)(((int64_t)row_l * a.k_sn + swz_k<D>(row_l, ph_l) * 8) * 2);
+    const uint32_t voff = (uint32_t)(((int64_t)row_l * a.v_sn + swz_v<D>(row_l, ph_l) * 8) * 2);
+    static_assert((RPI * NW) % 16 == 0, "a wave's loads must share their swizzle");
     auto load_tile = [&](int t, bf16 *Kd, bf16 *Vd) {
         const int key0 = t * BT;
         if (key0 + BT <= N) {
@@ -209,10 +209,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             for (int j = 0; j < NI; ++j) {
                 if (NINST % NW != 0 && wave + NW * j >= NINST) break;
                 const int row0 = RPI * (wave + NW * j);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(kb + koff[j]),
-                                                 (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(vb + voff[j]),
-                                                 (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
+                const int64_t jr = (int64_t)RPI * NW * j;  // rows between load 0 and load j
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(kb + jr * a.k_sn * 2 + koff),
+                    (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(vb + jr * a.v_sn * 2 + voff),
+                    (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
             }
         } else {
 #pragma unroll
