@@ -46,6 +46,26 @@ constexpr float kMInit = -1e30f;
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Direct global -> LDS load (global_load_lds_dwordx4): lane i of the wave
+// fetches 16 bytes from gptr into LDS at lds_base + 16 i (lds_base uniform,
+// held in M0).  Written in asm so that the compiler's wait bookkeeping does
+// not see it: while a builtin one is in flight the compiler waits for every
+// outstanding LDS read at each use (a full lgkmcnt(0)).  The instruction
+// writes no registers; its completion is waited for explicitly (s_waitcnt
+// 0) before the barrier that publishes the tile, and an extra outstanding
+// load only makes the compiler's own vmcnt waits stricter.  The s_nop is the
+// wait state between writing M0 and the load that reads it.
+__device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_base)
+                 : "memory", "m0");
+}
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+    return (uint32_t)(size_t)(const __attribute__((address_space(3))) void *)p;
+}
+
 __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *__restrict__ p) {
     i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) i16x4 *)(p));
@@ -200,8 +220,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const uint32_t koff = (uint32_t)(((int64_t)row_l * a.k_sn + swz_k<D>(row_l, ph_l) * 8) * 2);
     const uint32_t voff = (uint32_t)(((int64_t)row_l * a.v_sn + swz_v<D>(row_l, ph_l) * 8) * 2);
     static_assert((RPI * NW) % 16 == 0, "a wave's loads must share their swizzle");
+    const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_addr(lds));
     auto load_tile = [&](int t, bf16 *Kd, bf16 *Vd) {
         const int key0 = t * BT;
+        const uint32_t kd = lds0 + (uint32_t)(Kd - lds) * 2, vd = lds0 + (uint32_t)(Vd - lds) * 2;
         if (key0 + BT <= N) {
             const char *kb = (const char *)(kbase + (int64_t)key0 * a.k_sn);
             const char *vb = (const char *)(vbase + (int64_t)key0 * a.v_sn);
@@ -210,12 +232,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 if (NINST % NW != 0 && wave + NW * j >= NINST) break;
                 const int row0 = RPI * (wave + NW * j);
                 const int64_t jr = (int64_t)RPI * NW * j;  // rows between load 0 and load j
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(kb + jr * a.k_sn * 2 + koff),
-                    (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds(
-                    (const __attribute__((address_space(1))) void *)(vb + jr * a.v_sn * 2 + voff),
-                    (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
+                lds_dma16(kb + jr * a.k_sn * 2 + koff, kd + row0 * D * 2);
+                lds_dma16(vb + jr * a.v_sn * 2 + voff, vd + row0 * D * 2);
             }
         } else {
 #pragma unroll
@@ -226,10 +244,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 const int key = key0 + row < N ? key0 + row : N - 1;
                 const bf16 *kp = kbase + (int64_t)key * a.k_sn + swz_k<D>(row, ph) * 8;
                 const bf16 *vp = vbase + (int64_t)key * a.v_sn + swz_v<D>(row, ph) * 8;
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)kp,
-                                                 (__attribute__((address_space(3))) void *)(Kd + row0 * D), 16, 0, 0);
-                __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)vp,
-                                                 (__attribute__((address_space(3))) void *)(Vd + row0 * D), 16, 0, 0);
+                lds_dma16(kp, kd + row0 * D * 2);
+                lds_dma16(vp, vd + row0 * D * 2);
             }
         }
     };
@@ -240,36 +256,61 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
 
     // S^T for keys [32h, 32h+32) of a staged tile: s[kb][rb] holds keys
-    // kb*16+4g+r of the step, query column c16.
+    // kb*16+4g+r of the step, query column c16.  The K fragments of 32-dim
+    // step ks+1 are read while the products of step ks run (the scheduling
+    // groups fix that order).
     auto qk = [&](const bf16 *Kb, int h, f32x4 (&s)[NKB][RB]) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        bf16x8 A[KS][NKB];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) {
                 const int row = BN * h + kb * 16 + c16;
-                const bf16x8 A = *(const bf16x8 *)(Kb + row * D + swz_k<D>(row, ks * 4 + g) * 8);
+                A[ks][kb] = *(const bf16x8 *)(Kb + row * D + swz_k<D>(row, ks * 4 + g) * 8);
+            }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qreg[rb][ks],
+                    s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks][kb], qreg[rb][ks],
                                                                         s[kb][rb], 0, 0, 0);
-            }
+        // Scheduling groups (0x100: LDS reads, 0x008: matrix-core ops).
+        __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, NKB * RB, 0);
+        }
     };
-    // O^T += V^T P^T for keys [32h, 32h+32) of a staged V tile.
+    // O^T += V^T P^T for keys [32h, 32h+32) of a staged V tile; the V^T
+    // fragments of block db+2 are read while the products of block db run.
     auto pv = [&](const bf16 *Vb, int h, const bf16x8 (&pk)[RB], f32x4 (&o)[RB][DB]) {
         const int row1 = BN * h + 4 * g + (c16 >> 2), row2 = row1 + 16;
         const int half = (c16 & 1) * 4;
+        bf16x8 A[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             const int lch = 2 * db + ((c16 & 3) >> 1);
-            const bf16x8 A = concat(lds_read_tr(Vb + row1 * D + swz_v<D>(row1, lch) * 8 + half),
-                                    lds_read_tr(Vb + row2 * D + swz_v<D>(row2, lch) * 8 + half));
+            A[db] = concat(lds_read_tr(Vb + row1 * D + swz_v<D>(row1, lch) * 8 + half),
+                           lds_read_tr(Vb + row2 * D + swz_v<D>(row2, lch) * 8 + half));
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
-                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, pk[rb], o[rb][db], 0, 0, 0);
+                o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[db], pk[rb], o[rb][db], 0, 0, 0);
+        constexpr int AHEAD = 2;  // 16-dim blocks whose V^T reads are in flight
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            if (db + AHEAD < DB) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, RB, 0);
         }
     };
     // Visible-key test of the attention variant and the sink + recent set.
