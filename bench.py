@@ -220,7 +220,7 @@ def main() -> int:
     result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
                           "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
                           "traffic": traffic,
-                          "kernel": "attn_bf16_kernel<D=128, RB=3, BT=64, FULL_LAZY> + lazy_reduce_kernel"}
+                          "kernel": "attn_bf16_kernel<D=128, RB=3, BT=128, FULL_LAZY> + lazy_reduce_kernel"}
     del sout, slse
 
     # hybrid decode step: B8, context 100000, 64 layers (32 full + 32 streaming)

@@ -48,18 +48,27 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 
 // Direct global -> LDS load (global_load_lds_dwordx4): lane i of the wave
 // fetches 16 bytes from gptr into LDS at lds_base + 16 i (lds_base uniform,
-// held in M0).  Written in asm so that the compiler's wait bookkeeping does
+// passed in M0).  Written in asm so that the compiler's wait bookkeeping does
 // not see it: while a builtin one is in flight the compiler waits for every
 // outstanding LDS read at each use (a full lgkmcnt(0)).  The instruction
 // writes no registers; its completion is waited for explicitly (s_waitcnt
 // 0) before the barrier that publishes the tile, and an extra outstanding
-// load only makes the compiler's own vmcnt waits stricter.  The s_nop is the
-// wait state between writing M0 and the load that reads it.
+// load only makes the compiler's own vmcnt waits stricter.  M0 is saved and
+// restored around it (the compiler does not track M0 through asm); the
+// s_nops are the wait states between writing M0 and the instructions that
+// read it.
 __device__ __forceinline__ void lds_dma16(const void *gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_base)
-                 : "memory", "m0");
+    unsigned saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_nop 0\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(gptr), "s"(lds_base)
+        : "memory");
 }
 // LDS byte address of a pointer into a __shared__ array.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
@@ -521,7 +530,8 @@ __global__ void lazy_reduce_kernel(const float *rows, float *ratio, int BH, int 
     ratio[i] = acc / (float)W;
 }
 
-template <int D, int RB, int BT, int NW>
+// MODES: bit mask of the modes this configuration is built for.
+template <int D, int RB, int BT, int NW, int MODES>
 hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     const int64_t rows = (int64_t)a.N * a.G;
     const int brows = NW * 16 * RB;
@@ -529,25 +539,35 @@ hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     a.n_qtiles = (int)((rows + brows - 1) / brows);
     dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv));
     dim3 block(64 * NW);
-    switch (mode) {
-    case MODE_FULL:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL, NW>), grid, block, 0, st, a);
-        break;
-    case MODE_FULL_LAZY:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL_LAZY, NW>), grid, block, 0, st, a);
-        break;
-    default:
-        hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_STREAM, NW>), grid, block, 0, st, a);
-        break;
+    if constexpr ((MODES & (1 << MODE_FULL)) != 0) {
+        if (mode == MODE_FULL) {
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL, NW>), grid, block, 0, st, a);
+            return hipGetLastError();
+        }
     }
-    return hipGetLastError();
+    if constexpr ((MODES & (1 << MODE_FULL_LAZY)) != 0) {
+        if (mode == MODE_FULL_LAZY) {
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL_LAZY, NW>), grid, block, 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    if constexpr ((MODES & (1 << MODE_STREAM)) != 0) {
+        if (mode == MODE_STREAM) {
+            hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_STREAM, NW>), grid, block, 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
-    // 3 row blocks per wave and 64-key tiles: O (3*D/16 x 4), S^T (3 x 8),
-    // Q^T (3*D/16 x 2) and the rest fit 256 registers for two waves per SIMD.
-    return launch_cfg<D, 3, 64, 8>(a, mode, st);
+    // 3 row blocks per wave: O (3*D/16 x 4), S^T (3 x 8), Q^T (3*D/16 x 2)
+    // and the rest fit 256 registers for two waves per SIMD.  Full attention
+    // takes 128-key tiles (half the workgroup barriers per key); streaming,
+    // which keeps its raw scores, stays at 64 keys to fit its registers.
+    if (mode == MODE_STREAM) return launch_cfg<D, 3, 64, 8, 1 << MODE_STREAM>(a, mode, st);
+    return launch_cfg<D, 3, 128, 8, (1 << MODE_FULL) | (1 << MODE_FULL_LAZY)>(a, mode, st);
 }
 
 }  // namespace
