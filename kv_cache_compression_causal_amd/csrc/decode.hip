@@ -304,21 +304,45 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 }
 
 // Merge split partials: out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M);
-// lse = (M + log2 sum_s w_s) ln 2.
+// lse = (M + log2 sum_s w_s) ln 2.  One block per (batch, query head), one
+// thread per head dim.  The partials were written by workgroups on every XCD,
+// so each load is a round trip to the shared memory level: all loads of up
+// to CH splits are issued together, and chunks of CH splits are merged
+// online (a running max M with L, O rescaled when it grows).
 template <int D, typename T>
-__global__ __launch_bounds__(128) void decode_combine_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+    constexpr int CH = 16;
     const int bh = blockIdx.x;
     const int d = threadIdx.x;
-    const float *src = a.ws + (int64_t)bh * a.n_splits * (D + 2);
-    float M = kNegInf;
-    for (int s = 0; s < a.n_splits; ++s) M = fmaxf(M, src[s * (D + 2) + D]);
-    float L = 0.f, O = 0.f;
-    for (int s = 0; s < a.n_splits; ++s) {
-        const float w = src[s * (D + 2) + D + 1] * __builtin_amdgcn_exp2f(src[s * (D + 2) + D] - M);
-        L += w;
-        if (d < D) O += w * src[s * (D + 2) + d];
+    const int n = a.n_splits;
+    const float *src = a.ws + (int64_t)bh * n * (D + 2);
+    float M = kNegInf, L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < n; s0 += CH) {
+        float mv[CH], lv[CH], ov[CH];
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+            const int sp = s0 + i < n ? s0 + i : n - 1;
+            mv[i] = src[sp * (D + 2) + D];
+            lv[i] = src[sp * (D + 2) + D + 1];
+            ov[i] = src[sp * (D + 2) + d];
+        }
+        float Mc = M;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (s0 + i < n) Mc = fmaxf(Mc, mv[i]);
+        const float f = __builtin_amdgcn_exp2f(M - Mc);  // 0 while M is -inf
+        L *= f;
+        O *= f;
+#pragma unroll
+        for (int i = 0; i < CH; ++i)
+            if (s0 + i < n) {
+                const float w = lv[i] * __builtin_amdgcn_exp2f(mv[i] - Mc);
+                L += w;
+                O += w * ov[i];
+            }
+        M = Mc;
     }
-    if (d < D) ((T *)a.o)[(int64_t)bh * D + d] = (T)(O / L);
+    ((T *)a.o)[(int64_t)bh * D + d] = (T)(O / L);
     if (d == 0 && a.lse != nullptr) a.lse[bh] = (M + log2f(L)) * kLn2;
 }
 
@@ -347,7 +371,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
         dim3 grid((unsigned)a.n_splits, (unsigned)(a.B * a.Hkv));
         if (a.D == 64) {
             hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(256), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<64, bf16>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
+            hipLaunchKernelGGL((decode_combine_kernel<64, bf16>), dim3(a.B * a.Hq), dim3(64), 0, st, a);
         } else {
             hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, st, a);
             hipLaunchKernelGGL((decode_combine_kernel<128, bf16>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
@@ -356,7 +380,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
         dim3 grid((unsigned)a.n_splits, (unsigned)(a.B * a.Hq));
         if (a.D == 64) {
             hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(64), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<64, float>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
+            hipLaunchKernelGGL((decode_combine_kernel<64, float>), dim3(a.B * a.Hq), dim3(64), 0, st, a);
         } else {
             hipLaunchKernelGGL(decode_f32_kernel<128>, grid, dim3(64), 0, st, a);
             hipLaunchKernelGGL((decode_combine_kernel<128, float>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
