@@ -274,6 +274,42 @@ def main() -> int:
         del graph, qs, ks_, vs_, outs, lses, ws
         torch.cuda.empty_cache()
 
+    # Measured peaks: the matrix-core and HBM-read rates the chip delivers in
+    # practice (probe kernels of the library), next to the published peaks the
+    # roofline fractions use.
+    def best_ms(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        return best
+
+    blocks, iters = 2048, 2000
+    psink = torch.empty(blocks * 256, device=dev, dtype=torch.float32)
+    pfl = float(blocks) * 4 * iters * 8 * 16384
+    mfma_ms = best_ms(lambda: api.lt_probe_mfma_bf16(blocks, iters, psink, stream))
+    rbuf = torch.empty(4 << 30, device=dev, dtype=torch.uint8)
+    rsink = torch.zeros(8192, device=dev, dtype=torch.int32)
+    read_ms = best_ms(lambda: api.lt_probe_read(rbuf, 8192, rsink, stream))
+    result["measured_peaks"] = {
+        "mfma_bf16_tflops": round(pfl / (mfma_ms * 1e-3) / 1e12, 1),
+        "hbm_read_gbps": round(rbuf.numel() / (read_ms * 1e-3) / 1e9, 1),
+        "spec_mfma_bf16_tflops": PEAK_BF16 / 1e12, "spec_hbm_gbps": PEAK_HBM / 1e9,
+        "probes": "lt_probe_mfma_bf16: 2048 workgroups x 4 waves, 8 independent 16x16x32 bf16 "
+                  "MFMA chains per wave; lt_probe_read: one pass of 16-byte loads over 4 GiB (contiguous share per workgroup), "
+                  "8192 workgroups; best of 3"}
+    log(f"measured peaks: {result['measured_peaks']['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
+        f"{result['measured_peaks']['hbm_read_gbps']} GB/s read")
+    del rbuf, rsink, psink
+    torch.cuda.empty_cache()
+
     # The 64-layer LightTransfer-Test prefill: selection and KV bytes
     if not args.no_driver:
         from kv_cache_compression_causal_amd import driver
@@ -330,13 +366,49 @@ def main() -> int:
             flop += sum(4.0 * D * (int(p) + 1) for p in ps)
             flop += sum(2.0 * D * min(S + R, int(p) + 1) for p in ps if p >= N - W)
         cpu_tflops = flop / t_cpu / 1e12
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         result["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
-                                  "cores": oracle.threads(), "kind": "oracle",
+                                  "cores": oracle.threads(), "kind": "oracle", "cpu_model": cpu_model,
                                   "sample": f"{nrow} query rows of the qwen32k layer (the last W=128 rows "
                                             f"+ uniform random rows, random heads), full softmax row "
                                             f"materialised in fp64; {t_cpu:.1f} s; FLOP counted as "
                                             f"for the GPU (4*D*(i+1) per row + lazy numerator)"}
         log(f"oracle: {cpu_tflops * 1e3:.3f} GFLOP/s on {oracle.threads()} threads ({t_cpu:.1f} s)")
+        if not args.no_decode:
+            # The oracle's decode: batch element 0 of one full and one streaming
+            # layer of the decode step, extrapolated to the 64-layer step (x8
+            # batch, x32 layers of each kind); bytes counted as for the GPU.
+            dw = synth.DECODE100K
+            nfull = int(dw.extra["full_layers"])
+            t_layer, b_layer = {}, {}
+            for l in (0, nfull):
+                ql, kl, vl = synth.decode_layer(l, dw, device=dev)
+                qh = ql[:1].double().cpu().numpy()
+                kh = kl[:1].double().cpu().numpy()
+                vh = vl[:1].double().cpu().numpy()
+                del ql, kl, vl
+                c0 = time.perf_counter()
+                oracle.decode(qh, kh, vh)
+                t_layer[l] = time.perf_counter() - c0
+                b_layer[l] = 2 * dw.Hkv * kh.shape[2] * dw.D * 2 + 2 * dw.Hq * dw.D * 2
+                del qh, kh, vh
+            L = int(dw.extra["layers"])
+            t_step = dw.B * (nfull * t_layer[0] + (L - nfull) * t_layer[nfull])
+            b_step = dw.B * (nfull * b_layer[0] + (L - nfull) * b_layer[nfull])
+            result["cpu_baseline"]["decode"] = {
+                "value": round(b_step / t_step / 1e9, 3), "unit": "GB/s",
+                "sample": f"decode100k layers 0 (100000 rows) and {nfull} (1024 rows), batch element 0, "
+                          f"fp64 ({t_layer[0]:.2f} s + {t_layer[nfull]:.3f} s), extrapolated to "
+                          f"the 64-layer step at B8"}
+            log(f"oracle decode: {b_step / t_step / 1e9:.3f} GB/s")
 
     print(json.dumps(result), flush=True)
     return 0

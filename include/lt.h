@@ -181,6 +181,25 @@ int lt_lazy_queue_push_ratios(lt_lazy_queue *queue, int layer, const float *head
 int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
                           int *evicted_at_step, uint8_t *is_streaming);
 
+/*
+ * Measurement probes, not part of the path: the matrix-core and HBM-read
+ * rates the chip delivers in practice, reported next to the published peaks
+ * that roofline fractions are taken against.  Both are asynchronous on
+ * `stream`; the caller times them (e.g. with events on that stream).
+ *   lt_probe_mfma_bf16: `blocks` workgroups of 4 waves; each wave runs
+ *     `iters` rounds of 8 independent 16x16x32 bf16 matrix-core products
+ *     (16384 FLOP each), i.e. blocks*4*iters*8*16384 FLOP.  sink: device
+ *     fp32 [blocks*256], overwritten with meaningless values.
+ *   lt_probe_read: reads `bytes` of device memory at `buf` once (16-byte
+ *     aligned, bytes a multiple of 16) with `blocks` workgroups of 256
+ *     lanes.  sink: device u32 [blocks], written only on an unlikely value.
+ * Errors: LT_ERR_NULL (null pointer), LT_ERR_SHAPE (blocks < 1, iters < 1,
+ * bytes not a positive multiple of 16), LT_ERR_LAYOUT (buf not 16-byte
+ * aligned), LT_ERR_HIP (launch failure).
+ */
+int lt_probe_mfma_bf16(int blocks, int iters, float *sink, hipStream_t stream);
+int lt_probe_read(const void *buf, size_t bytes, int blocks, unsigned *sink, hipStream_t stream);
+
 /* Name of a status code, and the calling thread's last error message. */
 const char *lt_status_str(int status);
 const char *lt_last_error(void);

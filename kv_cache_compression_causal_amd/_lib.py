@@ -19,7 +19,7 @@ EXPORTS = (
     "lt_prefill_attn_lse_lazy", "lt_streaming_attn", "lt_hybrid_decode_workspace_bytes",
     "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
     "lt_lazy_queue_push", "lt_lazy_queue_push_ratios", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
-    "lt_last_error",
+    "lt_last_error", "lt_probe_mfma_bf16", "lt_probe_read",
 )
 
 
@@ -89,6 +89,10 @@ def lib() -> ctypes.CDLL:
     L.lt_status_str.restype = ctypes.c_char_p
     L.lt_last_error.argtypes = []
     L.lt_last_error.restype = ctypes.c_char_p
+    L.lt_probe_mfma_bf16.argtypes = [c_int, c_int, c_void_p, c_void_p]
+    L.lt_probe_mfma_bf16.restype = c_int
+    L.lt_probe_read.argtypes = [c_void_p, c_size_t, c_int, c_void_p, c_void_p]
+    L.lt_probe_read.restype = c_int
     _lib = L
     return L
 

@@ -186,3 +186,21 @@ def lt_select_lazy_layers(head_ratio, C: int):
         ev.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
         st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
     return score, ev, st
+
+
+def lt_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> float:
+    """Launch the matrix-core probe; returns the FLOP it performs (the caller
+    times it).  sink: float32 device tensor of at least blocks*256 elements."""
+    if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor of blocks*256 elements")
+    check(lib().lt_probe_mfma_bf16(int(blocks), int(iters), sink.data_ptr(), _stream(stream)))
+    return float(blocks) * 4 * iters * 8 * 16384
+
+
+def lt_probe_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None) -> int:
+    """Launch the read probe over all of buf; returns the bytes it reads."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < blocks:
+        raise ValueError("buf must be contiguous; sink an int32 tensor of >= blocks elements")
+    check(lib().lt_probe_read(buf.data_ptr(), nbytes, int(blocks), sink.data_ptr(), _stream(stream)))
+    return nbytes

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "liblt.so")
 ARCH = "gfx950"
 
-SOURCES = ["attn_bf16.hip", "attn_f32.hip", "decode.hip", "compact.hip", "lt_api.cpp",
+SOURCES = ["attn_bf16.hip", "attn_f32.hip", "decode.hip", "compact.hip", "probe.hip", "lt_api.cpp",
            "lazy_queue.cpp"]
 
 # -packed-fp32-ops: keep the compiler from emitting packed fp32 VALU ops.

@@ -213,4 +213,17 @@ int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64
     return ok();
 }
 
+int lt_probe_mfma_bf16(int blocks, int iters, float *sink, hipStream_t stream) {
+    if (sink == nullptr) return fail(LT_ERR_NULL, "sink is NULL");
+    if (blocks < 1 || iters < 1) return fail(LT_ERR_SHAPE, "blocks and iters must be >= 1");
+    return hip_status(lt::launch_mfma_probe(blocks, iters, sink, stream), "mfma probe launch");
+}
+
+int lt_probe_read(const void *buf, size_t bytes, int blocks, unsigned *sink, hipStream_t stream) {
+    if (buf == nullptr || sink == nullptr) return fail(LT_ERR_NULL, "buf/sink is NULL");
+    if (blocks < 1 || bytes == 0 || bytes % 16) return fail(LT_ERR_SHAPE, "bad probe sizes");
+    if (!aligned16(buf)) return fail(LT_ERR_LAYOUT, "buf not 16-byte aligned");
+    return hip_status(lt::launch_read_probe(buf, bytes, blocks, sink, stream), "read probe launch");
+}
+
 }  // extern "C"

@@ -68,5 +68,7 @@ struct CompactArgs {
     int B, Hkv, N, D, elem, S, R, rows_out;
 };
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
+hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t st);
+hipError_t launch_read_probe(const void *buf, size_t bytes, int blocks, unsigned *sink, hipStream_t st);
 
 }  // namespace lt

@@ -186,3 +186,16 @@ def test_kv_bytes_matches_oracle(L):
                                      (2, 3, 10, 64, 0, 4, 20)]:
         e = 2 if dt == 1 else 4
         assert api.lt_kv_bytes(B, Hkv, N, D, dt, S, R) == oracle.kv_bytes(B, Hkv, N, D, e, S, R)
+
+
+def test_probe_errors(L):
+    """The measurement probes validate before any launch (no GPU call here)."""
+    assert L.lt_probe_mfma_bf16(0, 1, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert L.lt_probe_mfma_bf16(1, 0, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert L.lt_probe_mfma_bf16(1, 1, None, None) == _lib.LT_ERR_NULL
+    assert L.lt_probe_read(None, 16, 1, GOOD, None) == _lib.LT_ERR_NULL
+    assert L.lt_probe_read(GOOD, 16, 1, None, None) == _lib.LT_ERR_NULL
+    assert L.lt_probe_read(GOOD, 15, 1, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert L.lt_probe_read(GOOD, 0, 1, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert L.lt_probe_read(GOOD, 16, 0, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert L.lt_probe_read(GOOD + 8, 16, 1, GOOD, None) == _lib.LT_ERR_LAYOUT
