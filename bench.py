@@ -339,6 +339,19 @@ def main() -> int:
         log(f"driver64: retained {res.retained_bytes[-1] / MiB:.0f} MiB of {L64 * res.full_bytes / MiB:.0f}, "
             f"peak {max(res.transient_bytes) / MiB:.0f} MiB")
         torch.cuda.empty_cache()
+        # The other eviction timing the pages describe: the laziest queued layer
+        # leaves before the current one is stored.
+        res_b = driver.run(layer_inputs, int(dw.extra["layers"]), int(dw.extra["capacity"]), dw.S, dw.R,
+                           dw.W, timing=False, policy=_lib.LT_EVICT_BEFORE_PUSH)
+        result["driver64"]["evict_before_push"] = {
+            "streaming_layers": [l for l in range(L64) if res_b.is_streaming[l]],
+            "evicted_at_step": res_b.evicted_at_step,
+            "kv_retained_final_MiB": res_b.retained_bytes[-1] / MiB,
+            "kv_peak_transient_MiB": max(res_b.transient_bytes) / MiB,
+        }
+        log(f"driver64 (evict before push): peak {max(res_b.transient_bytes) / MiB:.0f} MiB")
+        del res_b
+        torch.cuda.empty_cache()
 
     # CPU baseline: the oracle on a bounded row sample of the same workload
     if not args.no_cpu:

@@ -158,6 +158,21 @@ int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64
  */
 typedef struct lt_lazy_queue lt_lazy_queue;
 int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out);
+
+/*
+ * When the queue evicts.  The pages give two timings ([P4] Figure 2 caption:
+ * a layer leaves once the queue exceeds its capacity; [P1] solution 2: when
+ * the queue reaches capacity, the laziest layer leaves to free memory for
+ * the current one).
+ *   LT_EVICT_AFTER_PUSH (the default of lt_lazy_queue_create and
+ *     lt_select_lazy_layers): push, then evict while more than C are queued;
+ *     the current layer may leave at its own step.
+ *   LT_EVICT_BEFORE_PUSH: if C layers are already queued, evict the laziest
+ *     of them, then push; the current layer always enters (with C == 0 no
+ *     layer can be queued and each leaves at its own step).
+ */
+enum { LT_EVICT_AFTER_PUSH = 0, LT_EVICT_BEFORE_PUSH = 1 };
+int lt_lazy_queue_create_policy(int L, int C, int policy, lt_lazy_queue **out);
 int lt_lazy_queue_push(lt_lazy_queue *queue, int layer, double score, int *evicted);
 void lt_lazy_queue_destroy(lt_lazy_queue *queue);
 
@@ -180,6 +195,9 @@ int lt_lazy_queue_push_ratios(lt_lazy_queue *queue, int layer, const float *head
  */
 int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
                           int *evicted_at_step, uint8_t *is_streaming);
+/* The same with an eviction policy (LT_EVICT_AFTER_PUSH or _BEFORE_PUSH). */
+int lt_select_lazy_layers_policy(const float *head_ratio, int L, int n, int C, int policy,
+                                 double *layer_score, int *evicted_at_step, uint8_t *is_streaming);
 
 /*
  * Measurement probes, not part of the path: the matrix-core and HBM-read

@@ -13,13 +13,15 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblt.so")
 LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_LAYOUT, LT_ERR_WORKSPACE, LT_ERR_HIP, \
     LT_ERR_VALUE = range(8)
 LT_F32, LT_BF16 = 0, 1
+LT_EVICT_AFTER_PUSH, LT_EVICT_BEFORE_PUSH = 0, 1
 
 # Every symbol include/lt.h declares.
 EXPORTS = (
     "lt_prefill_attn_lse_lazy", "lt_streaming_attn", "lt_hybrid_decode_workspace_bytes",
     "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
     "lt_lazy_queue_push", "lt_lazy_queue_push_ratios", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
-    "lt_last_error", "lt_probe_mfma_bf16", "lt_probe_read",
+    "lt_last_error", "lt_probe_mfma_bf16", "lt_probe_read", "lt_lazy_queue_create_policy",
+    "lt_select_lazy_layers_policy",
 )
 
 
@@ -85,6 +87,12 @@ def lib() -> ctypes.CDLL:
     L.lt_select_lazy_layers.argtypes = [fp, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_double),
                                         ctypes.POINTER(c_int), ctypes.POINTER(ctypes.c_uint8)]
     L.lt_select_lazy_layers.restype = c_int
+    L.lt_lazy_queue_create_policy.argtypes = [c_int, c_int, c_int, ctypes.POINTER(c_void_p)]
+    L.lt_lazy_queue_create_policy.restype = c_int
+    L.lt_select_lazy_layers_policy.argtypes = [fp, c_int, c_int, c_int, c_int,
+                                               ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_int),
+                                               ctypes.POINTER(ctypes.c_uint8)]
+    L.lt_select_lazy_layers_policy.restype = c_int
     L.lt_status_str.argtypes = [c_int]
     L.lt_status_str.restype = ctypes.c_char_p
     L.lt_last_error.argtypes = []

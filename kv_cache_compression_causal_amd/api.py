@@ -135,11 +135,12 @@ def lt_kv_bytes(B: int, Hkv: int, N: int, D: int, dtype: int, S: int, R: int) ->
 
 
 class LazyQueue:
-    """lt_lazy_queue_create / _push / _destroy."""
+    """lt_lazy_queue_create_policy / _push / _destroy.  policy: LT_EVICT_AFTER_PUSH
+    (0, the default) or LT_EVICT_BEFORE_PUSH (1)."""
 
-    def __init__(self, L: int, C: int):
+    def __init__(self, L: int, C: int, policy: int = 0):
         h = ctypes.c_void_p()
-        check(lib().lt_lazy_queue_create(L, C, ctypes.byref(h)))
+        check(lib().lt_lazy_queue_create_policy(L, C, int(policy), ctypes.byref(h)))
         self._h = h
 
     def push(self, layer: int, score: float) -> int:
@@ -170,9 +171,10 @@ class LazyQueue:
             pass
 
 
-def lt_select_lazy_layers(head_ratio, C: int):
+def lt_select_lazy_layers(head_ratio, C: int, policy: int = 0):
     """head_ratio [L, n] (host, fp32).  Returns (layer_score [L] float64,
-    evicted_at_step [L] int32, is_streaming [L] uint8)."""
+    evicted_at_step [L] int32, is_streaming [L] uint8).  policy as for
+    LazyQueue (lt_select_lazy_layers_policy)."""
     hr = np.ascontiguousarray(np.asarray(head_ratio, dtype=np.float32))
     if hr.ndim != 2:
         raise ValueError("head_ratio must be [L, n]")
@@ -180,8 +182,8 @@ def lt_select_lazy_layers(head_ratio, C: int):
     score = np.empty(L, dtype=np.float64)
     ev = np.empty(L, dtype=np.int32)
     st = np.empty(L, dtype=np.uint8)
-    check(lib().lt_select_lazy_layers(
-        hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), L, n, C,
+    check(lib().lt_select_lazy_layers_policy(
+        hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), L, n, C, int(policy),
         score.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
         ev.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
         st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))

@@ -5,10 +5,12 @@
 // switched to the streaming version.  This bounds the prefill's KV at C full
 // layers plus streaming layers at every step.
 //
-// Readings the pages leave open: the queue pushes, then pops while its size
-// exceeds C (so the current layer may leave at its own step); equal ratios
-// evict the lower layer index first; a layer's score is the fp64 mean of its
-// per-(batch, head) ratios in index order.
+// Readings the pages leave open: by default the queue pushes, then pops
+// while its size exceeds C (so the current layer may leave at its own step);
+// the other timing the pages describe (evict the laziest queued layer before
+// pushing once C are queued) is a policy flag.  Equal ratios evict the lower
+// layer index first; a layer's score is the fp64 mean of its per-(batch,
+// head) ratios in index order.
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -36,8 +38,20 @@ inline bool above(const Entry &a, const Entry &b) {
 }  // namespace
 
 struct lt_lazy_queue {
-    int L, C, next;
+    int L, C, next, policy;
     std::vector<Entry> heap;  // binary max-heap under above()
+
+    // One step: layer e.layer arrives; returns the layer evicted, or -1.
+    int step(const Entry &e) {
+        if (policy == LT_EVICT_BEFORE_PUSH) {
+            if (C == 0) return e.layer;
+            const int v = (int)heap.size() == C ? pop().layer : -1;
+            push(e);
+            return v;
+        }
+        push(e);
+        return (int)heap.size() > C ? pop().layer : -1;
+    }
 
     void push(const Entry &e) {
         heap.push_back(e);
@@ -85,26 +99,30 @@ bool mean_of(const float *x, int n, double *out) {
 
 extern "C" {
 
-int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out) {
+int lt_lazy_queue_create_policy(int L, int C, int policy, lt_lazy_queue **out) {
     if (out == nullptr) return qfail(LT_ERR_NULL, "out is NULL");
     if (L < 1) return qfail(LT_ERR_SHAPE, "L must be >= 1");
     if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
+    if (policy != LT_EVICT_AFTER_PUSH && policy != LT_EVICT_BEFORE_PUSH)
+        return qfail(LT_ERR_VALUE, "unknown eviction policy");
     lt_lazy_queue *q = new (std::nothrow) lt_lazy_queue();
     if (q == nullptr) return qfail(LT_ERR_VALUE, "out of host memory");
-    q->L = L; q->C = C; q->next = 0;
+    q->L = L; q->C = C; q->next = 0; q->policy = policy;
     q->heap.reserve((size_t)C + 1);
     *out = q;
     return qfail(LT_OK, "");
+}
+
+int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out) {
+    return lt_lazy_queue_create_policy(L, C, LT_EVICT_AFTER_PUSH, out);
 }
 
 int lt_lazy_queue_push(lt_lazy_queue *q, int layer, double score, int *evicted) {
     if (q == nullptr || evicted == nullptr) return qfail(LT_ERR_NULL, "queue/evicted is NULL");
     if (layer != q->next) return qfail(LT_ERR_VALUE, "layers must be pushed in order");
     if (isnan(score) || isinf(score)) return qfail(LT_ERR_VALUE, "score must be finite");
-    q->push(Entry{score, layer});
+    *evicted = q->step(Entry{score, layer});
     q->next++;
-    *evicted = -1;
-    if ((int)q->heap.size() > q->C) *evicted = q->pop().layer;
     return qfail(LT_OK, "");
 }
 
@@ -122,32 +140,36 @@ int lt_lazy_queue_push_ratios(lt_lazy_queue *q, int layer, const float *head_rat
     return e;
 }
 
-int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
-                          int *evicted_at_step, uint8_t *is_streaming) {
+int lt_select_lazy_layers_policy(const float *head_ratio, int L, int n, int C, int policy,
+                                 double *layer_score, int *evicted_at_step, uint8_t *is_streaming) {
     if (head_ratio == nullptr || evicted_at_step == nullptr || is_streaming == nullptr)
         return qfail(LT_ERR_NULL, "NULL argument");
     if (L < 1 || n < 1) return qfail(LT_ERR_SHAPE, "L and n must be >= 1");
     if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
+    if (policy != LT_EVICT_AFTER_PUSH && policy != LT_EVICT_BEFORE_PUSH)
+        return qfail(LT_ERR_VALUE, "unknown eviction policy");
     std::vector<double> score((size_t)L);
     for (int l = 0; l < L; ++l)
         if (!mean_of(head_ratio + (size_t)l * n, n, &score[l]))
             return qfail(LT_ERR_VALUE, "head ratio is not finite");
     lt_lazy_queue q;
-    q.L = L; q.C = C; q.next = 0;
+    q.L = L; q.C = C; q.next = 0; q.policy = policy;
     q.heap.reserve((size_t)C + 1);
     for (int l = 0; l < L; ++l) is_streaming[l] = 0;
     for (int l = 0; l < L; ++l) {
-        q.push(Entry{score[l], l});
-        evicted_at_step[l] = -1;
-        if ((int)q.heap.size() > C) {
-            const int v = q.pop().layer;
-            evicted_at_step[l] = v;
-            is_streaming[v] = 1;
-        }
+        const int v = q.step(Entry{score[l], l});
+        evicted_at_step[l] = v;
+        if (v >= 0) is_streaming[v] = 1;
     }
     if (layer_score != nullptr)
         for (int l = 0; l < L; ++l) layer_score[l] = score[l];
     return qfail(LT_OK, "");
+}
+
+int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *layer_score,
+                          int *evicted_at_step, uint8_t *is_streaming) {
+    return lt_select_lazy_layers_policy(head_ratio, L, n, C, LT_EVICT_AFTER_PUSH, layer_score,
+                                        evicted_at_step, is_streaming);
 }
 
 }  // extern "C"

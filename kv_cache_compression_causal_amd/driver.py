@@ -6,7 +6,8 @@ Chinese write-up, "solution 2"):
   2. the per-head ratios go to the host; the layer score is their mean;
   3. the score enters the lazy-layer queue; if the queue holds more than C
      layers, the highest-score layer leaves and its KV cache is compacted to
-     the sink + recent rows and the full copy released.
+     the sink + recent rows and the full copy released (or, with eviction
+     before the push, the highest of the C already queued leaves first).
 The KV bytes held after each step (and while a layer's full KV is added,
 before the queue's decision) are tracked, so the peak prefill KV can be
 checked against C full layers + the rest streaming.
@@ -25,7 +26,7 @@ from typing import Callable, Dict, List, Optional, Tuple
 import torch
 
 from . import api, ops, synth
-from ._lib import LT_BF16, LT_F32
+from ._lib import LT_BF16, LT_EVICT_AFTER_PUSH, LT_EVICT_BEFORE_PUSH, LT_F32
 
 
 @dataclass
@@ -45,10 +46,14 @@ class DriverResult:
 
 
 def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], layers: int,
-        capacity: int, S: int, R: int, W: int, timing: bool = False) -> DriverResult:
+        capacity: int, S: int, R: int, W: int, timing: bool = False,
+        policy: int = LT_EVICT_AFTER_PUSH) -> DriverResult:
     """Run the layer stack.  ``layer_inputs(l)`` returns (q, k, v) for layer l
-    on the device; the layer's k, v are its KV cache."""
-    queue = api.LazyQueue(layers, capacity)
+    on the device; the layer's k, v are its KV cache.  policy: the queue's
+    eviction timing (LT_EVICT_AFTER_PUSH or LT_EVICT_BEFORE_PUSH).  With
+    eviction before the push the victim does not depend on the current layer,
+    so its KV counts as freed before the current layer's KV is stored."""
+    queue = api.LazyQueue(layers, capacity, policy)
     kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
     streaming_kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
     head_ratio, scores, evicted, retained, transient, times = [], [], [], [], [], []
@@ -79,9 +84,11 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
             times.append(e0.elapsed_time(e1))
         kv[l] = (k, v)
         del q
-        held = sum(stream_b if is_stream[x] else full_b for x in range(l)) + full_b
-        transient.append(held)
         ev, score = queue.push_ratios(l, r)
+        freed_first = policy == LT_EVICT_BEFORE_PUSH and 0 <= ev < l
+        held = sum(stream_b if (is_stream[x] or (freed_first and x == ev)) else full_b
+                   for x in range(l)) + full_b
+        transient.append(held)
         if ev >= 0:
             kf, vf = kv.pop(ev)
             streaming_kv[ev] = ops.compact(kf, vf, S, R)
@@ -100,6 +107,8 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
 def main(argv: Optional[List[str]] = None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--layers", type=int, default=None)
+    ap.add_argument("--evict-before-push", action="store_true",
+                    help="evict the laziest queued layer before pushing once the queue is full")
     args = ap.parse_args(argv)
     w = synth.DRIVER64
     L = args.layers or int(w.extra["layers"])
@@ -112,7 +121,8 @@ def main(argv: Optional[List[str]] = None) -> int:
 
     print(f"[driver] {L} layers of B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D}, capacity {C}",
           file=sys.stderr, flush=True)
-    res = run(inputs, L, C, w.S, w.R, w.W, timing=True)
+    policy = LT_EVICT_BEFORE_PUSH if args.evict_before_push else LT_EVICT_AFTER_PUSH
+    res = run(inputs, L, C, w.S, w.R, w.W, timing=True, policy=policy)
     srt = sorted(res.layer_score)
     gaps = [b - a for a, b in zip(srt, srt[1:])]
     MiB = 1 << 20
@@ -120,6 +130,7 @@ def main(argv: Optional[List[str]] = None) -> int:
     report = {
         "workload": f"driver64: {L} layers, B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D} bf16, "
                     f"S{w.S} R{w.R} W{w.W}, capacity {C}",
+        "eviction": "before push" if args.evict_before_push else "after push",
         "streaming_layers": [l for l in range(L) if res.is_streaming[l]],
         "full_layers": [l for l in range(L) if not res.is_streaming[l]],
         "evicted_at_step": res.evicted_at_step,

@@ -195,16 +195,25 @@ def layer_score(head_ratio_row: Sequence[float]) -> float:
     return acc / len(head_ratio_row)
 
 
-def select_lazy_layers(scores: Sequence[float], capacity: int) -> Tuple[List[int], List[int]]:
-    """Priority queue keyed by lazy ratio, updated after each layer.
+def select_lazy_layers(scores: Sequence[float], capacity: int,
+                       policy: str = "after") -> Tuple[List[int], List[int]]:
+    """Priority queue keyed by lazy ratio, updated after each layer
+    (LightTransfer project page, Figure 2 caption; Chinese write-up,
+    solution 2).
 
-    Layer l is pushed as (score, l); while the queue holds more than
-    ``capacity`` layers, the highest score leaves (equal scores: lower layer
-    index first) and becomes a streaming layer.  Returns
-    (evicted_at_step [L] with -1 for none, is_streaming [L] as 0/1)."""
+    policy "after" (the project page's timing): layer l is pushed as
+    (score, l); while the queue holds more than ``capacity`` layers, the
+    highest score leaves (equal scores: lower layer index first) and becomes a
+    streaming layer.  policy "before" (the write-up's "free memory for the
+    current layer"): when ``capacity`` layers are already queued, the highest
+    of them leaves first, then layer l is pushed; with capacity 0 every layer
+    leaves at its own step.  Returns (evicted_at_step [L] with -1 for none,
+    is_streaming [L] as 0/1)."""
     L = len(scores)
     if not (0 <= capacity <= L):
         raise ValueError("capacity must lie in [0, L]")
+    if policy not in ("after", "before"):
+        raise ValueError("policy must be 'after' or 'before'")
     heap: List[Tuple[float, int]] = []
     evicted = [-1] * L
     streaming = [0] * L
@@ -212,9 +221,16 @@ def select_lazy_layers(scores: Sequence[float], capacity: int) -> Tuple[List[int
         s = float(s)
         if math.isnan(s) or math.isinf(s):
             raise ValueError("scores must be finite")
-        heapq.heappush(heap, (-s, l))
-        if len(heap) > capacity:
-            _, victim = heapq.heappop(heap)
+        if policy == "before":
+            if capacity == 0:
+                victim = l
+            else:
+                victim = heapq.heappop(heap)[1] if len(heap) == capacity else -1
+                heapq.heappush(heap, (-s, l))
+        else:
+            heapq.heappush(heap, (-s, l))
+            victim = heapq.heappop(heap)[1] if len(heap) > capacity else -1
+        if victim >= 0:
             evicted[l] = victim
             streaming[victim] = 1
     return evicted, streaming
@@ -236,17 +252,22 @@ def kv_bytes(B: int, Hkv: int, N: int, D: int, elem: int, S: int, R: int) -> Tup
     return full, stream
 
 
-def kv_accounting(evicted_at_step: Sequence[int], full: int, stream: int) -> Dict[str, List[int]]:
+def kv_accounting(evicted_at_step: Sequence[int], full: int, stream: int,
+                  policy: str = "after") -> Dict[str, List[int]]:
     """Per-step KV bytes while prefill walks the layers.
 
     transient[l]: every layer so far at its current size plus layer l at full
-    size, before the queue's pop.  retained[l]: the same after the pop."""
+    size, before the queue's pop -- except that with eviction before the push
+    a victim from an earlier layer is already streaming (its memory is freed
+    for layer l).  retained[l]: the same after the pop."""
     L = len(evicted_at_step)
     is_stream = [False] * L
     retained, transient = [], []
     for l in range(L):
-        before = sum(stream if is_stream[x] else full for x in range(l)) + full
         ev = evicted_at_step[l]
+        if policy == "before" and 0 <= ev < l:
+            is_stream[ev] = True
+        before = sum(stream if is_stream[x] else full for x in range(l)) + full
         if ev >= 0:
             is_stream[ev] = True
         after = sum(stream if is_stream[x] else full for x in range(l + 1))

@@ -140,8 +140,9 @@ def test_status_strings(L):
         "LT_ERR_HIP", "LT_ERR_VALUE"]
 
 
+@pytest.mark.parametrize("policy", [_lib.LT_EVICT_AFTER_PUSH, _lib.LT_EVICT_BEFORE_PUSH])
 @pytest.mark.parametrize("seed", range(50))
-def test_select_matches_oracle_bit_exact(L, seed):
+def test_select_matches_oracle_bit_exact(L, seed, policy):
     from kv_cache_compression_causal_amd import api
     rnd = random.Random(seed)
     Lyr = rnd.randint(1, 64)
@@ -149,18 +150,28 @@ def test_select_matches_oracle_bit_exact(L, seed):
     C = rnd.randint(0, Lyr)
     hr = np.array([[rnd.choice([rnd.random(), 0.5, 0.25]) for _ in range(n)] for _ in range(Lyr)],
                   dtype=np.float32)
-    score, ev, st = api.lt_select_lazy_layers(hr, C)
+    score, ev, st = api.lt_select_lazy_layers(hr, C, policy)
     want_scores = [oracle.layer_score(row.astype(np.float64)) for row in hr]
     assert list(score) == want_scores
-    wev, wst = oracle.select_lazy_layers(want_scores, C)
+    wev, wst = oracle.select_lazy_layers(
+        want_scores, C, policy="before" if policy == _lib.LT_EVICT_BEFORE_PUSH else "after")
     assert list(ev) == wev and list(st) == wst
-    q = api.LazyQueue(Lyr, C)
+    q = api.LazyQueue(Lyr, C, policy)
     assert [q.push(l, s) for l, s in enumerate(want_scores)] == wev
     q.close()
-    q = api.LazyQueue(Lyr, C)
+    q = api.LazyQueue(Lyr, C, policy)
     pushed = [q.push_ratios(l, row) for l, row in enumerate(hr)]
     assert [e for e, _ in pushed] == wev and [s for _, s in pushed] == want_scores
     q.close()
+    if policy == _lib.LT_EVICT_AFTER_PUSH:  # the policy-free entry points are the default
+        n_ = ctypes.c_int()
+        s2, ev2, st2 = np.empty(Lyr), np.empty(Lyr, dtype=np.int32), np.empty(Lyr, dtype=np.uint8)
+        assert L.lt_select_lazy_layers(
+            hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), Lyr, n, C,
+            s2.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+            ev2.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
+            st2.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))) == 0
+        assert list(ev2) == wev
 
 
 def test_queue_errors(L):
@@ -178,6 +189,11 @@ def test_queue_errors(L):
         q.push(1, math.inf)  # not finite
     with pytest.raises(_lib.LtError):
         api.LazyQueue(3, 4)
+    with pytest.raises(_lib.LtError) as e:
+        api.LazyQueue(3, 1, 7)  # unknown policy
+    assert e.value.status == _lib.LT_ERR_VALUE
+    with pytest.raises(_lib.LtError):
+        api.lt_select_lazy_layers(np.zeros((3, 2), dtype=np.float32), 1, 2)
 
 
 def test_kv_bytes_matches_oracle(L):

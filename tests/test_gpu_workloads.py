@@ -71,10 +71,14 @@ def test_decode100k_full_size(layer):
         assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
 
 
-def test_driver_small_stack():
+@pytest.mark.parametrize("policy", ["after", "before"])
+def test_driver_small_stack(policy):
     """8 layers with the driver's sink/recency recipe at N=1024: per-layer ratios
     against the oracle, the queue bit for bit on the same fp32 ratios, the
-    end-to-end selection, and the KV accounting."""
+    end-to-end selection, and the KV accounting, for both eviction timings."""
+    from kv_cache_compression_causal_amd import _lib
+    lt_policy = _lib.LT_EVICT_BEFORE_PUSH if policy == "before" else _lib.LT_EVICT_AFTER_PUSH
+    print(f"driver small stack, eviction {policy} push", flush=True)
     w = synth.Workload("driver-small", 1, 1024, 10, 2, 128, torch.bfloat16, 4000, 4, 100, 32,
                        extra={"layers": 8, "capacity": 4})
     cache = {}
@@ -84,7 +88,7 @@ def test_driver_small_stack():
         cache[l] = (np64(q), np64(k), np64(v))
         return q, k, v
 
-    res = driver.run(inputs, 8, 4, w.S, w.R, w.W)
+    res = driver.run(inputs, 8, 4, w.S, w.R, w.W, policy=lt_policy)
     want_scores = []
     for l in range(8):
         qh, kh, vh = cache[l]
@@ -95,14 +99,14 @@ def test_driver_small_stack():
     # (i) the same fp32 ratios through the oracle's queue: identical, bit for bit
     gpu_scores = [oracle.layer_score(np.array(r, dtype=np.float32).astype(np.float64)) for r in res.head_ratio]
     assert gpu_scores == res.layer_score
-    ev, st = oracle.select_lazy_layers(gpu_scores, 4)
+    ev, st = oracle.select_lazy_layers(gpu_scores, 4, policy=policy)
     assert ev == res.evicted_at_step and st == res.is_streaming
     # (ii) end to end with the oracle's own ratios, when no two scores are within tolerance
     srt = sorted(want_scores)
     if min(b - a for a, b in zip(srt, srt[1:])) > 2 * TOL_BF16_RATIO:
-        ev2, _ = oracle.select_lazy_layers(want_scores, 4)
+        ev2, _ = oracle.select_lazy_layers(want_scores, 4, policy=policy)
         assert ev2 == res.evicted_at_step
-    acc = oracle.kv_accounting(res.evicted_at_step, res.full_bytes, res.stream_bytes)
+    acc = oracle.kv_accounting(res.evicted_at_step, res.full_bytes, res.stream_bytes, policy=policy)
     assert acc["retained"] == res.retained_bytes and acc["transient"] == res.transient_bytes
     full, stream = oracle.kv_bytes(1, 2, 1024, 128, 2, w.S, w.R)
     assert (res.full_bytes, res.stream_bytes) == (full, stream)

@@ -100,3 +100,98 @@ def test_kv_accounting_driver_workload():
     for l, t in enumerate(acc["transient"]):
         nf = min(l, 32) + 1
         assert t == nf * full + (l + 1 - nf) * stream
+
+
+# Eviction before the push (Chinese write-up, solution 2: when the queue is
+# full the laziest layer leaves to free memory for the current one).
+
+def scan_simulation_before(scores, C):
+    """With C layers held, remove the max by a linear scan (equal scores:
+    lower layer index), then add the current layer; C == 0 holds nothing."""
+    held, ev = [], []
+    for l, s in enumerate(scores):
+        e = -1
+        if C == 0:
+            e = l
+        else:
+            if len(held) == C:
+                best = max(held, key=lambda t: (t[0], -t[1]))
+                held.remove(best)
+                e = best[1]
+            held.append((s, l))
+        ev.append(e)
+    return ev
+
+
+def closed_form_kept_before(scores, C):
+    """The last layer always stays (for C >= 1), with the C-1 lowest of the
+    earlier layers under (score, -index); proof by induction on the steps."""
+    L = len(scores)
+    if C == 0:
+        return set()
+    order = sorted(range(L - 1), key=lambda l: (scores[l], -l))
+    return {L - 1} | set(order[:C - 1])
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_queue_before_random(seed):
+    rnd = random.Random(1000 + seed)
+    L = rnd.randint(1, 40)
+    C = rnd.randint(0, L)
+    scores = [rnd.choice([rnd.random(), round(rnd.random(), 1)]) for _ in range(L)]
+    ev, st = oracle.select_lazy_layers(scores, C, policy="before")
+    assert ev == scan_simulation_before(scores, C)
+    kept = {l for l in range(L) if not st[l]}
+    assert kept == closed_form_kept_before(scores, C)
+    assert sum(st) == L - C
+    if C >= 1:
+        assert all(ev[l] != l for l in range(L))  # the current layer always enters
+
+
+def test_queue_before_exhaustive_with_ties():
+    vals = (0.0, 0.5, 1.0)
+    for L in range(1, 7):
+        for scores in itertools.product(vals, repeat=L):
+            for C in range(0, L + 1):
+                ev, st = oracle.select_lazy_layers(list(scores), C, policy="before")
+                assert ev == scan_simulation_before(list(scores), C)
+
+
+def test_queue_before_edges():
+    scores = [0.3, 0.9, 0.1, 0.7, 0.5]
+    ev, st = oracle.select_lazy_layers(scores, 0, policy="before")
+    assert ev == [0, 1, 2, 3, 4] and st == [1] * 5
+    ev, st = oracle.select_lazy_layers(scores, 5, policy="before")
+    assert ev == [-1] * 5 and st == [0] * 5
+    # C = 2: step 2 evicts 1 (0.9 > 0.3); step 3 evicts 0 (0.3 > 0.1); step 4 evicts 3
+    ev, st = oracle.select_lazy_layers(scores, 2, policy="before")
+    assert ev == [-1, -1, 1, 0, 3]
+    # the two timings differ: after-push evicts the current layer 1 at step 2
+    ev_after, _ = oracle.select_lazy_layers(scores, 2)
+    assert ev_after == [-1, -1, 1, 3, 4]
+
+
+def test_queue_policy_rejected():
+    with pytest.raises(ValueError):
+        oracle.select_lazy_layers([0.1], 1, policy="sometimes")
+
+
+def test_kv_accounting_before_push():
+    """Same 64-layer workload with eviction before the push: the victim is
+    freed before the current layer is stored, so at step l >= C the KV is C
+    full layers plus l+1-C streaming ones; the peak is the final 4224 MiB
+    (32 full + 32 streaming) instead of 4348 MiB (33 full + 31 streaming)."""
+    MiB = 1 << 20
+    full, stream = oracle.kv_bytes(1, 8, 32768, 128, 2, 4, 1020)
+    scores = [random.Random(2).random() for _ in range(64)]
+    ev, st = oracle.select_lazy_layers(scores, 32, policy="before")
+    acc = oracle.kv_accounting(ev, full, stream, policy="before")
+    assert acc["retained"][-1] == 4224 * MiB
+    assert max(acc["transient"]) == 4224 * MiB
+    for l, t in enumerate(acc["transient"]):
+        nf = min(l + 1, 32)
+        assert t == nf * full + (l + 1 - nf) * stream
+    # with C = 0 every layer is converted at its own step: never two full layers
+    ev0, _ = oracle.select_lazy_layers(scores, 0, policy="before")
+    acc0 = oracle.kv_accounting(ev0, full, stream, policy="before")
+    assert all(t == full + l * stream for l, t in enumerate(acc0["transient"]))
