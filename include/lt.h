@@ -132,14 +132,32 @@ int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale,
 
 /*
  * Switch a layer's KV to the streaming version ([P1] solution 2; [P4]
- * Figure 2): copy rows [0,S) then [N-R,N) of every (b, kv head) of k_full /
- * v_full [B,Hkv,N,D] into rows 0..S+R-1 of k_stream / v_stream
- * [B,Hkv,>=S+R,D]; when N <= S+R all N rows are copied in order.  A byte
+ * Figure 2): copy the rows of positions [0,S) and [N-R,N) of every (b, kv
+ * head) of k_full / v_full [B,Hkv,N,D] into k_stream / v_stream
+ * [B,Hkv,>=min(N,S+R),D]: position p < S into slot p, a recent position p
+ * into slot S + (p-S) mod R (a ring of R slots, so that decode can append in
+ * place with lt_stream_cache_append); when N <= S+R every row p goes to slot
+ * p.  Attention over the cache does not depend on the slot order.  A byte
  * copy; the caller frees the full buffers afterwards.
  */
 int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream,
                             int B, int Hkv, int N, int D, int dtype, int S, int R,
                             hipStream_t stream);
+
+/*
+ * Decode-time append to a streaming cache ([P4] Introduction: converted
+ * layers keep attending to the sink and recent keys): write the new token's
+ * K and V rows, k_new / v_new [B,Hkv,D] contiguous (device), for position
+ * `pos` into slot pos (pos < S) or S + (pos-S) mod R of every (b, kv head)
+ * of k_stream / v_stream [B,Hkv,>=min(pos+1,S+R),D] -- over the oldest recent
+ * token once the ring is full.  The cache then holds the sink + recent set
+ * of position pos; decode it with kv_len = min(pos+1, S+R).  Same slot rule
+ * as lt_compact_kv_streaming.  Errors: LT_ERR_DTYPE, LT_ERR_SHAPE (S < 0,
+ * R < 1, pos < 0), LT_ERR_NULL, LT_ERR_LAYOUT (16-byte alignment), LT_ERR_HIP.
+ */
+int lt_stream_cache_append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
+                           int B, int Hkv, int D, int dtype, int S, int R, int64_t pos,
+                           hipStream_t stream);
 
 /*
  * (full, streaming) KV bytes of one layer: 2*B*Hkv*N*D*e and

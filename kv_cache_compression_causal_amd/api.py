@@ -128,6 +128,24 @@ def lt_compact_kv_streaming(k_full: torch.Tensor, v_full: torch.Tensor, k_stream
                                         _stream(stream)))
 
 
+def lt_stream_cache_append(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new: torch.Tensor,
+                           v_new: torch.Tensor, S: int, R: int, pos: int, stream=None) -> None:
+    """k_new, v_new [B, Hkv, D] contiguous: the token at position pos; written
+    into its slot of the streaming cache [B, Hkv, >=min(pos+1, S+R), D]."""
+    B, Hkv, rows, D = k_stream.shape
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) \
+            or v_stream.shape != k_stream.shape:
+        raise ValueError("append shape mismatch")
+    if rows < min(pos + 1, S + R):
+        raise ValueError("streaming cache has too few rows for this position")
+    _same_dtype(k_stream, v_stream, k_new, v_new)
+    check(lib().lt_stream_cache_append(_view(k_stream), _view(v_stream), k_new.data_ptr(),
+                                       v_new.data_ptr(), B, Hkv, D, _dtype_code(k_stream), S, R,
+                                       int(pos), _stream(stream)))
+
+
 def lt_kv_bytes(B: int, Hkv: int, N: int, D: int, dtype: int, S: int, R: int) -> Tuple[int, int]:
     full, stream = ctypes.c_int64(), ctypes.c_int64()
     check(lib().lt_kv_bytes(B, Hkv, N, D, dtype, S, R, ctypes.byref(full), ctypes.byref(stream)))

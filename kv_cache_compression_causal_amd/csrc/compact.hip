@@ -2,8 +2,11 @@
 // Chinese write-up, "solution 2"; project page, Figure 2 caption): keep the
 // S sink rows and the R most recent rows of every (batch, KV head), i.e. the
 // sink + recent key set of the last query, and drop the rest.  A byte copy
-// in 16-byte chunks: output row r < S comes from row r, row r >= S from row
-// N - R + (r - S); with N <= S + R all N rows are copied in order.
+// in 16-byte chunks.  Slot r < S holds position r; the recent positions sit
+// on a ring of R slots, position p in slot S + (p - S) mod R, so that the
+// decode steps that follow can write each new token over the oldest recent
+// one (append_kernel); with N <= S + R all N rows are copied in order.
+// Attention does not depend on the slot order.
 #include "lt_internal.h"
 
 namespace lt {
@@ -24,7 +27,14 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
         const int r = (int)(rem / chunks_per_row);
         const int ch = (int)(rem % chunks_per_row);
         const int b = bh / a.Hkv, h = bh % a.Hkv;
-        const int src_row = (all_rows || r < a.S) ? r : a.N - a.R + (r - a.S);
+        int src_row = r;
+        if (!all_rows && r >= a.S) {
+            // the recent position p in [N-R, N) whose ring slot is r
+            const int base = a.N - a.R;
+            int m = (r - base) % a.R;
+            if (m < 0) m += a.R;
+            src_row = base + m;
+        }
         const char *src;
         char *dst;
         if (which == 0) {
@@ -38,7 +48,34 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     }
 }
 
+// Write the new token's K and V rows (k_new, v_new [B, Hkv, D] contiguous)
+// into slot `slot` of every (batch, KV head) of the streaming cache.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+    const int chunks_per_row = a.D * a.elem / 16;
+    const int64_t total = (int64_t)a.B * a.Hkv * chunks_per_row * 2;
+    for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int which = (int)(idx / (total / 2));  // 0 = K, 1 = V
+        const int64_t rem = idx % (total / 2);
+        const int bh = (int)(rem / chunks_per_row), ch = (int)(rem % chunks_per_row);
+        const int b = bh / a.Hkv, h = bh % a.Hkv;
+        const char *src = (const char *)(which == 0 ? a.kn : a.vn) + ((int64_t)bh * a.D) * a.elem;
+        char *dst = which == 0
+                        ? (char *)a.ks + ((int64_t)b * a.ks_sb + (int64_t)h * a.ks_sh + a.slot * a.ks_sn) * a.elem
+                        : (char *)a.vs + ((int64_t)b * a.vs_sb + (int64_t)h * a.vs_sh + a.slot * a.vs_sn) * a.elem;
+        *(uint4 *)(dst + ch * 16) = *(const uint4 *)(src + ch * 16);
+    }
+}
+
 }  // namespace
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t st) {
+    const int64_t total = (int64_t)a.B * a.Hkv * (a.D * a.elem / 16) * 2;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
     const int64_t total = (int64_t)a.B * a.Hkv * a.rows_out * (a.D * a.elem / 16) * 2;

@@ -201,6 +201,26 @@ int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt
     return hip_status(lt::launch_compact(a, stream), "compaction launch");
 }
 
+int lt_stream_cache_append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
+                           int B, int Hkv, int D, int dtype, int S, int R, int64_t pos,
+                           hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hkv < 1) return fail(LT_ERR_SHAPE, "B and Hkv must be >= 1");
+    if (S < 0 || R < 1 || pos < 0) return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, pos >= 0");
+    if (k_new == nullptr || v_new == nullptr) return fail(LT_ERR_NULL, "k_new/v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(LT_ERR_LAYOUT, "k_new/v_new not 16-byte aligned");
+    int e;
+    if ((e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype))) return e;
+    lt::AppendArgs a{};
+    a.kn = k_new; a.vn = v_new; a.ks = k_stream.data; a.vs = v_stream.data;
+    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
+    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
+    a.B = B; a.Hkv = Hkv; a.D = D; a.elem = elem_size(dtype);
+    a.slot = pos < S ? pos : S + (pos - S) % R;
+    return hip_status(lt::launch_append(a, stream), "append launch");
+}
+
 int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64_t *full_bytes,
                 int64_t *stream_bytes) {
     if (full_bytes == nullptr || stream_bytes == nullptr) return fail(LT_ERR_NULL, "output is NULL");

@@ -68,6 +68,15 @@ struct CompactArgs {
     int B, Hkv, N, D, elem, S, R, rows_out;
 };
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
+
+struct AppendArgs {
+    const void *kn, *vn;  // [B,Hkv,D] contiguous
+    void *ks, *vs;
+    int64_t ks_sb, ks_sh, ks_sn, vs_sb, vs_sh, vs_sn;
+    int B, Hkv, D, elem;
+    int64_t slot;
+};
+hipError_t launch_append(const AppendArgs &a, hipStream_t st);
 hipError_t launch_mfma_probe(int blocks, int iters, float *sink, hipStream_t st);
 hipError_t launch_read_probe(const void *buf, size_t bytes, int blocks, unsigned *sink, hipStream_t st);
 

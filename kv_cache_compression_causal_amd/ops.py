@@ -50,10 +50,21 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
-def compact(k_full: torch.Tensor, v_full: torch.Tensor, S: int, R: int, stream=None):
+def compact(k_full: torch.Tensor, v_full: torch.Tensor, S: int, R: int, stream=None,
+            slots: Optional[int] = None):
+    """Streaming cache of min(N, S+R) rows (or `slots` >= that many, e.g. S+R
+    for a cache that decode will keep appending to)."""
     B, Hkv, N, D = k_full.shape
-    rows = min(N, S + R)
+    rows = min(N, S + R) if slots is None else max(slots, min(N, S + R))
     ks = torch.empty(B, Hkv, rows, D, device=k_full.device, dtype=k_full.dtype)
     vs = torch.empty_like(ks)
     api.lt_compact_kv_streaming(k_full, v_full, ks, vs, S, R, stream)
     return ks, vs
+
+
+def stream_append(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new: torch.Tensor,
+                  v_new: torch.Tensor, S: int, R: int, pos: int, stream=None) -> int:
+    """Append the token at position pos; returns the kv_len to decode with."""
+    api.lt_stream_cache_append(k_stream, v_stream, k_new.contiguous(), v_new.contiguous(), S, R, pos,
+                               stream)
+    return min(pos + 1, S + R)

@@ -236,13 +236,33 @@ def select_lazy_layers(scores: Sequence[float], capacity: int,
     return evicted, streaming
 
 
+def stream_slot(p: int, S: int, R: int) -> int:
+    """Slot of position p in a streaming cache of S + R slots: the sinks keep
+    their place, the recent positions go round a ring of R slots.  (The pages
+    are silent on slot order; attention does not depend on it, and this order
+    lets later tokens be appended in place.)"""
+    return p if p < S else S + (p - S) % R
+
+
 def streaming_rows(N: int, S: int, R: int) -> List[int]:
-    """Rows a streaming KV cache keeps: the sinks [0, S) then the recent
-    [N-R, N); every row when N <= S + R.  This is the sink + recent set of the
-    last query, N-1."""
+    """Positions a streaming KV cache of N tokens keeps, listed by slot: the
+    sinks [0, S) and the recent [N-R, N) (the sink + recent set of the last
+    query, N-1), position p in slot stream_slot(p); every row, in order, when
+    N <= S + R."""
     if N <= S + R:
         return list(range(N))
-    return list(range(S)) + list(range(N - R, N))
+    rows = [-1] * (S + R)
+    for p in list(range(S)) + list(range(N - R, N)):
+        rows[stream_slot(p, S, R)] = p
+    return rows
+
+
+def stream_append(rows: List[int], pos: int, S: int, R: int) -> List[int]:
+    """The positions of a streaming cache (listed by slot, -1 = empty) after
+    the token at position pos is written to its slot."""
+    out = list(rows) + [-1] * max(0, S + R - len(rows))
+    out[stream_slot(pos, S, R)] = pos
+    return out
 
 
 def kv_bytes(B: int, Hkv: int, N: int, D: int, elem: int, S: int, R: int) -> Tuple[int, int]:

@@ -215,3 +215,17 @@ def test_probe_errors(L):
     assert L.lt_probe_read(GOOD, 0, 1, GOOD, None) == _lib.LT_ERR_SHAPE
     assert L.lt_probe_read(GOOD, 16, 0, GOOD, None) == _lib.LT_ERR_SHAPE
     assert L.lt_probe_read(GOOD + 8, 16, 1, GOOD, None) == _lib.LT_ERR_LAYOUT
+
+
+def test_stream_append_errors(L):
+    f = L.lt_stream_cache_append
+    bf = _lib.LT_BF16
+    assert f(view(), view(), GOOD, GOOD, 2, 2, 128, 5, 4, 60, 10, None) == _lib.LT_ERR_DTYPE
+    assert f(view(), view(), GOOD, GOOD, 2, 2, 96, bf, 4, 60, 10, None) == _lib.LT_ERR_DTYPE
+    assert f(view(), view(), GOOD, GOOD, 0, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_SHAPE
+    assert f(view(), view(), GOOD, GOOD, 2, 2, 128, bf, -1, 60, 10, None) == _lib.LT_ERR_SHAPE
+    assert f(view(), view(), GOOD, GOOD, 2, 2, 128, bf, 4, 0, 10, None) == _lib.LT_ERR_SHAPE
+    assert f(view(), view(), GOOD, GOOD, 2, 2, 128, bf, 4, 60, -1, None) == _lib.LT_ERR_SHAPE
+    assert f(view(), view(), None, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_NULL
+    assert f(view(), view(), GOOD + 8, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_LAYOUT
+    assert f(view(ptr=GOOD + 8), view(), GOOD, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_LAYOUT

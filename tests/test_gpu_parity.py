@@ -125,6 +125,33 @@ def test_compaction_bit_exact(N, S, R, dtype):
     assert torch.equal(vs.cpu(), v[:, :, idx, :])
 
 
+@pytest.mark.parametrize("N0,T,S,R,dtype", [(300, 70, 4, 60, torch.bfloat16), (20, 50, 4, 30, torch.bfloat16),
+                                            (100, 40, 0, 16, torch.float32)])
+def test_streaming_decode_with_appends(N0, T, S, R, dtype):
+    """Prefill a layer of N0 tokens, compact it to a streaming cache of S+R
+    slots, then decode T more tokens, appending each one first: every step
+    equals the oracle's streaming attention of that token over the whole
+    sequence (sink + recent keys)."""
+    from kv_cache_compression_causal_amd import api
+    print(f"streaming decode with appends N0={N0} T={T} S={S} R={R} {dtype}", flush=True)
+    B, Hq, Hkv, D = 2, 10, 2, 128
+    N = N0 + T
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, 91, dtype)
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, streaming=True, full=False)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    ks, vs = ops.compact(kd[:, :, :N0].contiguous(), vd[:, :, :N0].contiguous(), S, R, slots=S + R)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, S + R, DEV)
+    to, tl, _ = _tol(dtype)
+    for pos in range(N0, N):
+        kv_len = ops.stream_append(ks, vs, kd[:, :, pos], vd[:, :, pos], S, R, pos)
+        out = torch.empty(B, Hq, D, device=DEV, dtype=dtype)
+        lse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+        api.lt_hybrid_decode_attn(qd[:, :, pos].contiguous(), ks, vs, kv_len, out, lse, ws)
+        torch.cuda.synchronize()
+        assert_close(f"out@{pos}", np64(out), ref["sout"][:, :, pos], to)
+        assert_close(f"lse@{pos}", np64(lse), ref["slse"][:, :, pos], tl)
+
+
 def test_lazy_ratio_equals_streaming_lse_gap():
     """Per-row lazy ratio = exp(LSE_stream - LSE_full): two kernels, one identity."""
     B, N, Hq, Hkv, D, S, R, W = 1, 700, 10, 2, 128, 4, 100, 64

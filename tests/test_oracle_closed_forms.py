@@ -149,10 +149,15 @@ def test_streaming_decode_on_compacted_cache_equals_streaming_row():
     q, k, v = _rand((1, 4, N, 8), 24, 2.0), _rand((1, 2, N, 8), 25), _rand((1, 2, N, 8), 26)
     st = oracle.prefill(q, k, v, S=S, R=R, streaming=True, full=False)
     idx = oracle.streaming_rows(N, S, R)
-    assert idx == list(range(S)) + list(range(N - R, N))
-    d = oracle.decode(q[:, :, N - 1], k[:, :, idx], v[:, :, idx])
+    assert sorted(idx) == list(range(S)) + list(range(N - R, N))
+    srt = sorted(idx)
+    d = oracle.decode(q[:, :, N - 1], k[:, :, srt], v[:, :, srt])
     assert np.array_equal(d["out"], st["sout"][:, :, N - 1])
     assert np.array_equal(d["lse"], st["slse"][:, :, N - 1])
+    # in the cache's own (ring) slot order: equal up to summation order
+    d2 = oracle.decode(q[:, :, N - 1], k[:, :, idx], v[:, :, idx])
+    np.testing.assert_allclose(d2["out"], d["out"], atol=1e-12)
+    np.testing.assert_allclose(d2["lse"], d["lse"], atol=1e-12)
 
 
 def test_decode_slot_order_irrelevant():
@@ -167,8 +172,30 @@ def test_decode_slot_order_irrelevant():
 def test_streaming_rows_edge_cases():
     assert oracle.streaming_rows(10, 4, 20) == list(range(10))
     assert oracle.streaming_rows(24, 4, 20) == list(range(24))
-    assert oracle.streaming_rows(25, 4, 20) == [0, 1, 2, 3] + list(range(5, 25))
-    assert oracle.streaming_rows(25, 0, 3) == [22, 23, 24]
+    # position 24 wraps round the ring of 20 recent slots to slot 4
+    assert oracle.streaming_rows(25, 4, 20) == [0, 1, 2, 3, 24] + list(range(5, 24))
+    assert oracle.streaming_rows(25, 0, 3) == [24, 22, 23]
+    assert [oracle.stream_slot(p, 4, 20) for p in (0, 3, 4, 23, 24, 43, 44)] == [0, 3, 4, 23, 4, 23, 4]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_stream_append_keeps_the_window(seed):
+    """Compaction of N0 tokens then appends up to position P: the cache holds
+    exactly the sink + recent set of P (positions [0, S) and (P-R, P]), and
+    appends from an empty cache reproduce compaction's layout slot by slot."""
+    rnd = np.random.default_rng(seed)
+    S, R = int(rnd.integers(0, 6)), int(rnd.integers(1, 12))
+    N0, T = int(rnd.integers(1, 40)), int(rnd.integers(1, 40))
+    rows = oracle.streaming_rows(N0, S, R)
+    for pos in range(N0, N0 + T):
+        rows = oracle.stream_append(rows, pos, S, R)
+        want = set(range(min(S, pos + 1))) | set(range(max(S, pos + 1 - R), pos + 1))
+        assert {p for p in rows if p >= 0} == want
+    fresh = []
+    for pos in range(N0 + T):
+        fresh = oracle.stream_append(fresh, pos, S, R)
+    n = min(N0 + T, S + R)
+    assert fresh[:n] == oracle.streaming_rows(N0 + T, S, R)
 
 
 def test_argument_errors():
