@@ -178,10 +178,10 @@ typedef struct lt_lazy_queue lt_lazy_queue;
 int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out);
 
 /*
- * When the queue evicts.  The pages give two timings ([P4] Figure 2 caption:
- * a layer leaves once the queue exceeds its capacity; [P1] solution 2: when
- * the queue reaches capacity, the laziest layer leaves to free memory for
- * the current one).
+ * When the queue evicts.  The pages give two timings ([P1] solution 2: a
+ * layer leaves once more layers are queued than the threshold; [P4] Figure 2
+ * caption: once the queue has reached its capacity, the laziest layer leaves,
+ * freeing memory for the current one).
  *   LT_EVICT_AFTER_PUSH (the default of lt_lazy_queue_create and
  *     lt_select_lazy_layers): push, then evict while more than C are queued;
  *     the current layer may leave at its own step.

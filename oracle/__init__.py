@@ -201,13 +201,14 @@ def select_lazy_layers(scores: Sequence[float], capacity: int,
     (LightTransfer project page, Figure 2 caption; Chinese write-up,
     solution 2).
 
-    policy "after" (the project page's timing): layer l is pushed as
-    (score, l); while the queue holds more than ``capacity`` layers, the
-    highest score leaves (equal scores: lower layer index first) and becomes a
-    streaming layer.  policy "before" (the write-up's "free memory for the
-    current layer"): when ``capacity`` layers are already queued, the highest
-    of them leaves first, then layer l is pushed; with capacity 0 every layer
-    leaves at its own step.  Returns (evicted_at_step [L] with -1 for none,
+    policy "after" (the write-up's timing: a layer leaves once more layers
+    are queued than the threshold): layer l is pushed as (score, l); while the
+    queue holds more than ``capacity`` layers, the highest score leaves (equal
+    scores: lower layer index first) and becomes a streaming layer.  policy
+    "before" (the project page's timing: once the queue is full, the laziest
+    layer leaves to make room for the current one): when ``capacity`` layers
+    are already queued, the highest of them leaves first, then layer l is
+    pushed; with capacity 0 every layer leaves at its own step.  Returns (evicted_at_step [L] with -1 for none,
     is_streaming [L] as 0/1)."""
     L = len(scores)
     if not (0 <= capacity <= L):

@@ -102,7 +102,7 @@ def test_kv_accounting_driver_workload():
         assert t == nf * full + (l + 1 - nf) * stream
 
 
-# Eviction before the push (Chinese write-up, solution 2: when the queue is
+# Eviction before the push (project page, Figure 2 caption: when the queue is
 # full the laziest layer leaves to free memory for the current one).
 
 def scan_simulation_before(scores, C):
