@@ -28,7 +28,10 @@ Readings where the pages are silent (each is listed in the design doc):
     the current layer can be evicted at its own step; equal scores evict the
     lower layer index first;
   * a layer's score is the mean of its per-head ratios over (batch, head);
-  * a streaming cache keeps rows [0, S) and [N-R, N), sinks first.
+  * a streaming cache keeps rows [0, S) and [N-R, N), sinks in their own
+    slots and the recent rows in ring order (stream_slot);
+  * offline selection averages each layer's score over the prompts (fp64,
+    prompt order) before taking the top half.
 
 Parity pins: tests/test_oracle_*.py (brute force in 50-digit arithmetic,
 torch fp64 library routines, closed forms, invariants, exhaustive queue
@@ -235,6 +238,41 @@ def select_lazy_layers(scores: Sequence[float], capacity: int,
             evicted[l] = victim
             streaming[victim] = 1
     return evicted, streaming
+
+
+def select_offline(prompt_scores: Sequence[Sequence[float]],
+                   capacity: int) -> Tuple[List[float], List[int]]:
+    """Offline lazy-layer selection (press-release page, "LightTransfer
+    method", steps 1-3): measure every layer's lazy ratio on a set of prompts,
+    call the layers with the highest ratios redundant and make them streaming
+    layers.  The page fixes the share (50%) but not how the prompts are
+    combined; here a layer's score is the mean of its per-prompt scores,
+    summed in fp64 in prompt order.  ``capacity`` layers stay full: the
+    L - capacity highest scores become streaming (equal scores: the lower
+    layer index first, as in the queue).  Returns (mean score [L],
+    is_streaming [L] as 0/1)."""
+    P = len(prompt_scores)
+    if P < 1:
+        raise ValueError("need at least one prompt")
+    L = len(prompt_scores[0])
+    if L < 1 or any(len(row) != L for row in prompt_scores):
+        raise ValueError("every prompt needs one score per layer")
+    if not (0 <= capacity <= L):
+        raise ValueError("capacity must lie in [0, L]")
+    mean = []
+    for l in range(L):
+        acc = 0.0
+        for p in range(P):
+            x = float(prompt_scores[p][l])
+            if math.isnan(x) or math.isinf(x):
+                raise ValueError("scores must be finite")
+            acc += x
+        mean.append(acc / P)
+    order = sorted(range(L), key=lambda l: (-mean[l], l))
+    streaming = [0] * L
+    for l in order[:L - capacity]:
+        streaming[l] = 1
+    return mean, streaming
 
 
 def stream_slot(p: int, S: int, R: int) -> int:
