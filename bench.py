@@ -352,6 +352,34 @@ def main() -> int:
         log(f"driver64 (evict before push): peak {max(res_b.transient_bytes) / MiB:.0f} MiB")
         del res_b
         torch.cuda.empty_cache()
+        # Offline selection: the same layers on several prompts, mean score, top half streaming.
+        P_off = 4
+        log(f"running offline selection over {P_off} prompts")
+
+        def prompt_inputs(p, l):
+            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=dev, prompt=p)
+            return ql, kl, vl
+
+        off = driver.offline(prompt_inputs, P_off, L64, int(dw.extra["capacity"]), dw.S, dw.R, dw.W,
+                             timing=True)
+        off_flop = prefill_flop(dw.B, dw.Hq, dw.N, dw.D) + lazy_flop(dw.B, dw.Hq, dw.N, dw.D, dw.S, dw.R,
+                                                                    dw.W)
+        mean_ms = sum(off.prefill_ms) / len(off.prefill_ms)
+        result["offline4"] = {
+            "workload": "offline4: 4 synthetic prompts through the 64 driver layers (per-layer sink scale "
+                        "and recency bias shared by all prompts), mean layer score over prompts, capacity 32",
+            "streaming_layers": [l for l in range(L64) if off.is_streaming[l]],
+            "differs_from_test_time": [sum(a != b for a, b in zip(off.is_streaming, tt))
+                                       for tt in off.test_time_streaming],
+            "prefill_launches": len(off.prefill_ms),
+            "prefill_ms_mean": round(mean_ms, 4),
+            "prefill_tflops": round(off_flop / (mean_ms * 1e-3) / 1e12, 2),
+            "wall_s": round(off.wall_s, 2),
+        }
+        log(f"offline4: {result['offline4']['prefill_tflops']} TFLOP/s per launch, layers differing from "
+            f"each prompt's test-time choice: {result['offline4']['differs_from_test_time']}")
+        del off
+        torch.cuda.empty_cache()
 
     # CPU baseline: the oracle on a bounded row sample of the same workload
     if not args.no_cpu:

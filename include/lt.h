@@ -16,7 +16,8 @@
  *        streaming KV by evicting the highest-ratio layer on overflow.
  *   [P3] Press-release page (wuwenjie.xyz): "LightTransfer method" -- the
  *        lazy ratio sums the attention weights from queries to the initial
- *        and the recent keys.
+ *        and the recent keys; offline, the layers are measured on a set of
+ *        prompts and the highest-ratio half replaced.
  *   [P4] LightTransfer project page: "Introduction" (lazy layers become
  *        streaming attention with a constant-size KV cache); Figure 2 caption
  *        (queue of (lazy ratio, layer index) updated after every layer; the
@@ -216,6 +217,23 @@ int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *
 /* The same with an eviction policy (LT_EVICT_AFTER_PUSH or _BEFORE_PUSH). */
 int lt_select_lazy_layers_policy(const float *head_ratio, int L, int n, int C, int policy,
                                  double *layer_score, int *evicted_at_step, uint8_t *is_streaming);
+
+/*
+ * Offline lazy-layer selection ([P3] "LightTransfer method", steps 1-3: the
+ * lazy ratio of every layer is measured on a set of prompts and the layers
+ * with the highest ratios are replaced by streaming attention).
+ * head_ratio [P][L][n] host fp32: the n per-(batch, head) lazy ratios of
+ * layer l on prompt p (the lazy_ratio output of lt_prefill_attn_lse_lazy).
+ * A layer's per-prompt score is the mean of its n ratios (fp64, index
+ * order); its offline score the mean of those over the P prompts (fp64,
+ * prompt order), written to layer_score [L] if not NULL.  The L - C layers
+ * with the highest offline scores get is_streaming [L] = 1 (equal scores:
+ * the lower layer index first), the other C stay full.  Host-only.  Errors:
+ * LT_ERR_NULL, LT_ERR_SHAPE (P, L or n < 1), LT_ERR_VALUE (C outside
+ * [0, L], a ratio not finite); outputs are untouched on error.
+ */
+int lt_select_offline(const float *head_ratio, int P, int L, int n, int C, double *layer_score,
+                      uint8_t *is_streaming);
 
 /*
  * Measurement probes, not part of the path: the matrix-core and HBM-read

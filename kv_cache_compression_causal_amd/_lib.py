@@ -21,7 +21,7 @@ EXPORTS = (
     "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
     "lt_lazy_queue_push", "lt_lazy_queue_push_ratios", "lt_lazy_queue_destroy", "lt_select_lazy_layers", "lt_status_str",
     "lt_last_error", "lt_probe_mfma_bf16", "lt_probe_read", "lt_lazy_queue_create_policy",
-    "lt_select_lazy_layers_policy", "lt_stream_cache_append",
+    "lt_select_lazy_layers_policy", "lt_stream_cache_append", "lt_select_offline",
 )
 
 
@@ -96,6 +96,9 @@ def lib() -> ctypes.CDLL:
     L.lt_stream_cache_append.argtypes = [LtView, LtView, c_void_p, c_void_p, c_int, c_int, c_int, c_int,
                                          c_int, c_int, c_int64, c_void_p]
     L.lt_stream_cache_append.restype = c_int
+    L.lt_select_offline.argtypes = [fp, c_int, c_int, c_int, c_int, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_uint8)]
+    L.lt_select_offline.restype = c_int
     L.lt_status_str.argtypes = [c_int]
     L.lt_status_str.restype = ctypes.c_char_p
     L.lt_last_error.argtypes = []

@@ -208,6 +208,22 @@ def lt_select_lazy_layers(head_ratio, C: int, policy: int = 0):
     return score, ev, st
 
 
+def lt_select_offline(head_ratio, C: int):
+    """head_ratio [P, L, n] (host, fp32): per-(batch, head) lazy ratios of
+    every layer on every prompt.  Returns (layer_score [L] float64, the mean
+    over prompts; is_streaming [L] uint8)."""
+    hr = np.ascontiguousarray(np.asarray(head_ratio, dtype=np.float32))
+    if hr.ndim != 3:
+        raise ValueError("head_ratio must be [P, L, n]")
+    P, L, n = hr.shape
+    score = np.empty(L, dtype=np.float64)
+    st = np.empty(L, dtype=np.uint8)
+    check(lib().lt_select_offline(hr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), P, L, n, C,
+                                  score.ctypes.data_as(ctypes.POINTER(ctypes.c_double)),
+                                  st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
+    return score, st
+
+
 def lt_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None) -> float:
     """Launch the matrix-core probe; returns the FLOP it performs (the caller
     times it).  sink: float32 device tensor of at least blocks*256 elements."""

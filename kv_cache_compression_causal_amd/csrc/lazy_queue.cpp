@@ -16,6 +16,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -170,6 +171,37 @@ int lt_select_lazy_layers(const float *head_ratio, int L, int n, int C, double *
                           int *evicted_at_step, uint8_t *is_streaming) {
     return lt_select_lazy_layers_policy(head_ratio, L, n, C, LT_EVICT_AFTER_PUSH, layer_score,
                                         evicted_at_step, is_streaming);
+}
+
+// Offline selection (press-release page, "LightTransfer method"): the score
+// of layer l is the mean over prompts of its per-prompt score (each the
+// fp64 mean of that prompt's per-(batch, head) ratios), summed in prompt
+// order; the L - C highest become streaming layers, ties to the lower index.
+int lt_select_offline(const float *head_ratio, int P, int L, int n, int C, double *layer_score,
+                      uint8_t *is_streaming) {
+    if (head_ratio == nullptr || is_streaming == nullptr) return qfail(LT_ERR_NULL, "NULL argument");
+    if (P < 1 || L < 1 || n < 1) return qfail(LT_ERR_SHAPE, "P, L and n must be >= 1");
+    if (C < 0 || C > L) return qfail(LT_ERR_VALUE, "capacity must lie in [0, L]");
+    std::vector<double> mean((size_t)L, 0.0);
+    for (int l = 0; l < L; ++l) {
+        double acc = 0.0;
+        for (int p = 0; p < P; ++p) {
+            double sc;
+            if (!mean_of(head_ratio + ((size_t)p * L + l) * n, n, &sc))
+                return qfail(LT_ERR_VALUE, "head ratio is not finite");
+            acc += sc;
+        }
+        mean[l] = acc / (double)P;
+    }
+    std::vector<int> order((size_t)L);
+    for (int l = 0; l < L; ++l) order[l] = l;
+    std::sort(order.begin(), order.end(),
+              [&](int a, int b) { return above(Entry{mean[a], a}, Entry{mean[b], b}); });
+    for (int l = 0; l < L; ++l) is_streaming[l] = 0;
+    for (int i = 0; i < L - C; ++i) is_streaming[order[i]] = 1;
+    if (layer_score != nullptr)
+        for (int l = 0; l < L; ++l) layer_score[l] = mean[l];
+    return qfail(LT_OK, "");
 }
 
 }  // extern "C"

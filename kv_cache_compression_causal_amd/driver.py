@@ -13,6 +13,7 @@ before the queue's decision) are tracked, so the peak prefill KV can be
 checked against C full layers + the rest streaming.
 
 Run the 64-layer workload:  python -m kv_cache_compression_causal_amd.driver
+Offline selection over P prompts:  python -m kv_cache_compression_causal_amd.driver --offline P
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ import time
 from dataclasses import dataclass, field
 from typing import Callable, Dict, List, Optional, Tuple
 
+import numpy as np
 import torch
 
 from . import api, ops, synth
@@ -104,16 +106,98 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
                         full_b, stream_b, times, time.perf_counter() - t_start)
 
 
+@dataclass
+class OfflineResult:
+    prompts: int
+    layers: int
+    capacity: int
+    head_ratio: List[List[List[float]]]     # [P][L][B*Hq]
+    prompt_score: List[List[float]]         # [P][L] fp64 mean of each layer's ratios on each prompt
+    layer_score: List[float]                # [L] mean over prompts
+    is_streaming: List[int]                 # offline selection
+    test_time_streaming: List[List[int]]    # [P][L]: the queue's choice on each prompt alone
+    prefill_ms: List[float] = field(default_factory=list)
+    wall_s: float = 0.0
+
+
+def offline(prompt_inputs: Callable[[int, int], Tuple[torch.Tensor, torch.Tensor, torch.Tensor]],
+            prompts: int, layers: int, capacity: int, S: int, R: int, W: int,
+            timing: bool = False) -> OfflineResult:
+    """Offline selection (press-release page, "LightTransfer method"): run
+    every prompt through every layer's prefill + lazy ratio (the same kernels
+    as at test time), then lt_select_offline keeps the ``capacity`` layers
+    with the lowest mean score full.  ``prompt_inputs(p, l)`` returns (q, k,
+    v) of layer l on prompt p.  For comparison each prompt's test-time queue
+    decision on its own ratios is reported too."""
+    ratios: List[List[List[float]]] = []
+    times: List[float] = []
+    out = lse = rows = ratio = None
+    t_start = time.perf_counter()
+    for p in range(prompts):
+        per_layer = []
+        for l in range(layers):
+            q, k, v = prompt_inputs(p, l)
+            B, Hq, N, D = q.shape
+            if out is None or out.shape != q.shape or out.dtype != q.dtype:
+                out = torch.empty_like(q)
+                lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+                rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+                ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+            if timing:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
+            if timing:
+                e1.record()
+            per_layer.append(ratio.reshape(-1).cpu().numpy())
+            if timing:
+                times.append(e0.elapsed_time(e1))
+            del q, k, v
+        ratios.append(per_layer)
+    hr = np.stack([np.stack(pl) for pl in ratios])          # [P, L, n] fp32
+    layer_score, st = api.lt_select_offline(hr, capacity)
+    prompt_score, test_time = [], []
+    for p in range(prompts):
+        sc, _, st_p = api.lt_select_lazy_layers(hr[p], capacity)
+        prompt_score.append([float(x) for x in sc])
+        test_time.append([int(x) for x in st_p])
+    return OfflineResult(prompts, layers, capacity, [[[float(x) for x in r] for r in pl] for pl in ratios],
+                         prompt_score, [float(x) for x in layer_score], [int(x) for x in st], test_time,
+                         times, time.perf_counter() - t_start)
+
+
 def main(argv: Optional[List[str]] = None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--evict-before-push", action="store_true",
                     help="evict the laziest queued layer before pushing once the queue is full")
+    ap.add_argument("--offline", type=int, default=0, metavar="P",
+                    help="offline selection over P synthetic prompts instead of the test-time queue")
     args = ap.parse_args(argv)
     w = synth.DRIVER64
     L = args.layers or int(w.extra["layers"])
     C = int(w.extra["capacity"]) if args.layers is None else L // 2
     dev = torch.device("cuda:0")
+    if args.offline > 0:
+        print(f"[driver] offline selection: {args.offline} prompts x {L} layers, capacity {C}",
+              file=sys.stderr, flush=True)
+
+        def prompt_inputs(p, l):
+            q, k, v, _, _ = synth.driver_layer(l, w, device=dev, prompt=p)
+            return q, k, v
+
+        off = offline(prompt_inputs, args.offline, L, C, w.S, w.R, w.W, timing=True)
+        print(json.dumps({
+            "workload": f"offline: {args.offline} prompts x {L} layers, B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} "
+                        f"D{w.D} bf16, S{w.S} R{w.R} W{w.W}, capacity {C}",
+            "streaming_layers": [l for l in range(L) if off.is_streaming[l]],
+            "layer_score": off.layer_score,
+            "differs_from_test_time": [sum(a != b for a, b in zip(off.is_streaming, tt))
+                                       for tt in off.test_time_streaming],
+            "prefill_ms_mean": sum(off.prefill_ms) / len(off.prefill_ms),
+            "wall_s": off.wall_s}), flush=True)
+        return 0
 
     def inputs(l):
         q, k, v, _, _ = synth.driver_layer(l, w, device=dev)

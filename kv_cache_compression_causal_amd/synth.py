@@ -16,6 +16,9 @@ contexts up to 100K tokens; real prompts and weights are not used):
             scaled by s_l ~ U[0,4]; the last 1020 keys shifted by b_l ~ U[0,2]
             times the unit direction of the group's mean query; (s_l, b_l)
             from numpy default_rng(4); queue capacity 32
+  offline4  4 prompts through the 64 driver layers: prompt p of layer l is
+            seeded 4000+l+100000p, the layer's (s_l, b_l) shared by all
+            prompts (prompt 0 is driver64 itself); capacity 32
   decode100k bf16, B8, context 100000, 64 layers of Hq40 Hkv8 D128, seed 5;
             layers 0..31 full (100000 rows), 32..63 streaming (1024 rows)
 """
@@ -99,14 +102,16 @@ def driver_layer_params(layers: int = 64, seed: int = 4) -> Tuple[np.ndarray, np
 
 
 def driver_layer(l: int, w: Workload = DRIVER64, device="cpu", sink_tokens: int = 4,
-                 recent: Optional[int] = None):
+                 recent: Optional[int] = None, prompt: int = 0):
     """Layer l of the 64-layer driver: q, k, v of the qwen32k shape, seed
-    4000+l; sink keys x s_l; keys of the last ``recent`` (default R) positions
-    + b_l * unit(mean of the group's queries over positions and heads)."""
+    4000+l (+ 100000 * prompt for further prompts through the same layers);
+    sink keys x s_l; keys of the last ``recent`` (default R) positions
+    + b_l * unit(mean of the group's queries over positions and heads).
+    (s_l, b_l) belong to the layer and are the same for every prompt."""
     s_all, b_all = driver_layer_params(int(w.extra.get("layers", 64)))
     s_l, b_l = float(s_all[l]), float(b_all[l])
     R = w.R if recent is None else recent
-    g = _gen(w.seed + l, device)
+    g = _gen(w.seed + l + 100000 * prompt, device)
     q = torch.randn(w.B, w.Hq, w.N, w.D, generator=g, device=device, dtype=torch.float32)
     k = torch.randn(w.B, w.Hkv, w.N, w.D, generator=g, device=device, dtype=torch.float32)
     v = torch.randn(w.B, w.Hkv, w.N, w.D, generator=g, device=device, dtype=torch.float32)

@@ -196,6 +196,50 @@ def test_queue_errors(L):
         api.lt_select_lazy_layers(np.zeros((3, 2), dtype=np.float32), 1, 2)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_select_offline_matches_oracle_bit_exact(L, seed):
+    """lt_select_offline against the oracle on the same fp32 ratios: the mean
+    scores bit for bit and the same streaming set (ties included)."""
+    from kv_cache_compression_causal_amd import api
+    rnd = random.Random(1000 + seed)
+    P, Lyr, n = rnd.randint(1, 6), rnd.randint(1, 64), rnd.randint(1, 40)
+    C = rnd.randint(0, Lyr)
+    hr = np.array([[[rnd.choice([rnd.random(), 0.5, 0.25]) for _ in range(n)] for _ in range(Lyr)]
+                   for _ in range(P)], dtype=np.float32)
+    score, st = api.lt_select_offline(hr, C)
+    per_prompt = [[oracle.layer_score(row.astype(np.float64)) for row in hr[p]] for p in range(P)]
+    want_score, want_st = oracle.select_offline(per_prompt, C)
+    assert list(score) == want_score
+    assert list(st) == want_st
+    if P == 1:  # one prompt: the set the push-then-pop queue keeps
+        _, _, st_q = api.lt_select_lazy_layers(hr[0], C)
+        assert list(st_q) == want_st
+
+
+def test_select_offline_errors(L):
+    from kv_cache_compression_causal_amd import api
+    ok = np.full((2, 3, 4), 0.25, dtype=np.float32)
+    for bad_C in (-1, 4):
+        with pytest.raises(_lib.LtError) as e:
+            api.lt_select_offline(ok, bad_C)
+        assert e.value.status == _lib.LT_ERR_VALUE
+    nan = ok.copy()
+    nan[1, 2, 3] = np.nan
+    st = np.full(3, 7, dtype=np.uint8)
+    with pytest.raises(_lib.LtError) as e:
+        api.lt_select_offline(nan, 1)
+    assert e.value.status == _lib.LT_ERR_VALUE
+    fp = ctypes.POINTER(ctypes.c_float)
+    u8 = ctypes.POINTER(ctypes.c_uint8)
+    assert L.lt_select_offline(nan.ctypes.data_as(fp), 2, 3, 4, 1, None,
+                               st.ctypes.data_as(u8)) == _lib.LT_ERR_VALUE
+    assert list(st) == [7, 7, 7]  # untouched on error
+    assert L.lt_select_offline(ok.ctypes.data_as(fp), 0, 3, 4, 1, None,
+                               st.ctypes.data_as(u8)) == _lib.LT_ERR_SHAPE
+    assert L.lt_select_offline(None, 2, 3, 4, 1, None, st.ctypes.data_as(u8)) == _lib.LT_ERR_NULL
+    assert L.lt_select_offline(ok.ctypes.data_as(fp), 2, 3, 4, 1, None, None) == _lib.LT_ERR_NULL
+
+
 def test_kv_bytes_matches_oracle(L):
     from kv_cache_compression_causal_amd import api
     for (B, Hkv, N, D, dt, S, R) in [(1, 8, 32768, 128, 1, 4, 1020), (8, 8, 100000, 128, 1, 4, 1020),

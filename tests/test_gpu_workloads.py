@@ -110,3 +110,46 @@ def test_driver_small_stack(policy):
     assert acc["retained"] == res.retained_bytes and acc["transient"] == res.transient_bytes
     full, stream = oracle.kv_bytes(1, 2, 1024, 128, 2, w.S, w.R)
     assert (res.full_bytes, res.stream_bytes) == (full, stream)
+
+
+@pytest.mark.gpu
+def test_offline_selection_small_stack():
+    """Offline selection over 3 prompts of an 8-layer stack at N=1024: every
+    prompt's per-layer ratios against the oracle, the selection bit for bit on
+    the same fp32 ratios, and end to end on the oracle's ratios when the mean
+    scores are far enough apart."""
+    print("offline selection, 3 prompts x 8 layers", flush=True)
+    w = synth.Workload("driver-small", 1, 1024, 10, 2, 128, torch.bfloat16, 4000, 4, 100, 32,
+                       extra={"layers": 8, "capacity": 4})
+    P, Lyr, C = 3, 8, 4
+    cache = {}
+
+    def inputs(p, l):
+        q, k, v, _, _ = synth.driver_layer(l, w, device=DEV, recent=w.R, prompt=p)
+        cache[p, l] = (np64(q), np64(k), np64(v))
+        return q, k, v
+
+    res = driver.offline(inputs, P, Lyr, C, w.S, w.R, w.W)
+    want = []
+    for p in range(P):
+        row = []
+        for l in range(Lyr):
+            qh, kh, vh = cache[p, l]
+            ref = oracle.prefill(qh, kh, vh, S=w.S, R=w.R, W=w.W, full=False)
+            np.testing.assert_allclose(np.array(res.head_ratio[p][l]), ref["lazy_ratio"].reshape(-1),
+                                       atol=TOL_BF16_RATIO)
+            row.append(oracle.layer_score(ref["lazy_ratio"].reshape(-1)))
+        want.append(row)
+    # (i) the library's fp32 ratios through the oracle: identical, bit for bit
+    gpu = [[oracle.layer_score(np.array(r, dtype=np.float32).astype(np.float64)) for r in res.head_ratio[p]]
+           for p in range(P)]
+    assert gpu == res.prompt_score
+    mean, st = oracle.select_offline(gpu, C)
+    assert mean == res.layer_score and st == res.is_streaming
+    for p in range(P):
+        assert oracle.select_lazy_layers(gpu[p], C)[1] == res.test_time_streaming[p]
+    # (ii) end to end with the oracle's own ratios, when no two means are within tolerance
+    mean_ref, st_ref = oracle.select_offline(want, C)
+    srt = sorted(mean_ref)
+    if min(b - a for a, b in zip(srt, srt[1:])) > 2 * TOL_BF16_RATIO:
+        assert st_ref == res.is_streaming
