@@ -185,6 +185,71 @@ def decode(q, k_cache, v_cache, scale: Optional[float] = None, lib=None) -> Dict
     return {"out": out, "lse": lse}
 
 
+def prefill_varlen(q, k, v, seq_lens: Sequence[int], S: int = 0, R: int = 1, W: int = 0,
+                   scale: Optional[float] = None, streaming: bool = False, full: bool = True,
+                   lib=None) -> Dict[str, np.ndarray]:
+    """A padded batch of sequences of different lengths: sequence b is its
+    first seq_lens[b] positions, and the method runs on it alone (nothing in
+    the pages couples the sequences of a batch).  Same outputs as prefill()
+    in the padded [B, H, N] layout; entries at or past a sequence's length are
+    NaN (no value).  Lazy ratio: each sequence observes its last
+    min(W, seq_lens[b]) queries; lazy_rows[b, h, k] is row seq_lens[b] - W + k
+    (NaN for rows before position 0) and lazy_ratio their mean (NaN for an
+    empty sequence)."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, Hq, N, D = q.shape
+    res: Dict[str, np.ndarray] = {}
+    if full:
+        res["out"] = np.full((B, Hq, N, D), np.nan)
+        res["lse"] = np.full((B, Hq, N), np.nan)
+    if streaming:
+        res["sout"] = np.full((B, Hq, N, D), np.nan)
+        res["slse"] = np.full((B, Hq, N), np.nan)
+    if W > 0:
+        res["lazy_rows"] = np.full((B, Hq, W), np.nan)
+        res["lazy_ratio"] = np.full((B, Hq), np.nan)
+    for b in range(B):
+        n = int(seq_lens[b])
+        if not (0 <= n <= N):
+            raise ValueError("sequence lengths must lie in [0, N]")
+        if n == 0:
+            continue
+        w = min(W, n)
+        one = prefill(q[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n], S=S, R=R, W=w,
+                      scale=scale, streaming=streaming, full=full, lib=lib)
+        for key in ("out", "sout"):
+            if key in one:
+                res[key][b, :, :n] = one[key][0]
+        for key in ("lse", "slse"):
+            if key in one:
+                res[key][b, :, :n] = one[key][0]
+        if w > 0:
+            res["lazy_rows"][b, :, W - w:] = one["lazy_rows"][0]
+            res["lazy_ratio"][b] = one["lazy_ratio"][0]
+    return res
+
+
+def decode_varlen(q, k_cache, v_cache, kv_lens: Sequence[int], scale: Optional[float] = None,
+                  lib=None) -> Dict[str, np.ndarray]:
+    """Decode over caches of different lengths: sequence b attends to rows
+    [0, kv_lens[b]) of its cache, alone.  An empty context has no softmax:
+    out = 0 and lse = -inf (the conventions of an empty sum)."""
+    q = _f64(q)
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(kv_lens[b])
+        if n < 0 or n > k_cache.shape[2]:
+            raise ValueError("kv_lens must lie in [0, rows]")
+        if n == 0:
+            continue
+        one = decode(q[b:b + 1], _f64(k_cache[b:b + 1, :, :n]), _f64(v_cache[b:b + 1, :, :n]),
+                     scale=scale, lib=lib)
+        out[b], lse[b] = one["out"][0], one["lse"][0]
+    return {"out": out, "lse": lse}
+
+
 # ---------------------------------------------------------------------------
 # Host-side selection (pure Python; small inputs by nature: one entry per layer)
 # ---------------------------------------------------------------------------
