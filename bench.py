@@ -1,6 +1,6 @@
 """Benchmark of the LightTransfer-Test hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-driver] [--no-cpu]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-driver] [--no-cpu] [--no-varlen]
 
 Headline leg (the step): one LightTransfer-Test layer at the qwen32k shape
 (B1 N32768 Hq40 Hkv8 D128 bf16, keys of tokens 0..3 x3, S4 R1020 W128):
@@ -13,8 +13,11 @@ Other legs, reported beside it: the same prefill without the lazy ratio
 (its overhead), streaming attention on the same tensors, one hybrid decode
 step at B8 / 100000-token context over 64 layers (32 full, 32 streaming at
 1024 rows; one distinct buffer per layer; the 64 calls are captured once in
-a HIP graph and replayed), and the 64-layer LightTransfer-Test prefill
-(selected layers, eviction order, KV bytes).
+a HIP graph and replayed), the 64-layer LightTransfer-Test prefill
+(selected layers, eviction order, KV bytes) and offline selection over four
+prompts, and variable-length batches: prefill over prompts of 32K/24K/16K/8K
+tokens padded to 32K, and the decode step with eight contexts from 100000
+down to 12500 tokens (lengths read per sequence on the device).
 
 roofline: the prefill+lazy kernel, FLOP per launch over its mean duration
 from HIP events on the launch stream, against the 2.5 PFLOP/s dense bf16
@@ -78,6 +81,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-driver", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=98304,
@@ -223,6 +227,29 @@ def main() -> int:
                           "kernel": "attn_bf16_kernel<D=128, RB=3, BT=128, FULL_LAZY> + lazy_reduce_kernel"}
     del sout, slse
 
+    # Variable-length batch: four prompts of 32K, 24K, 16K and 8K tokens padded to 32K.
+    if not args.no_varlen:
+        vw, vlens = synth.QWEN32K_VARLEN, synth.QWEN32K_VARLEN_LENS
+        log("generating the variable-length batch")
+        vq, vk, vv = synth.workload_qkv(vw, device=dev)
+        vout = torch.empty_like(vq)
+        vlse = torch.empty(vw.B, vw.Hq, vw.N, device=dev, dtype=torch.float32)
+        vrows = torch.empty(vw.B, vw.Hq, vw.W, device=dev, dtype=torch.float32)
+        vratio = torch.empty(vw.B, vw.Hq, device=dev, dtype=torch.float32)
+        vlens_d = torch.tensor(vlens, device=dev, dtype=torch.int32)
+        v_ms = timed(lambda: api.lt_prefill_attn_lse_lazy_varlen(vq, vk, vv, vout, vlse, vlens_d, vw.S, vw.R,
+                                                                 vw.W, vrows, vratio, 0.0, stream), K)
+        v_fl = sum(prefill_flop(1, vw.Hq, n, vw.D) + lazy_flop(1, vw.Hq, n, vw.D, vw.S, vw.R, vw.W)
+                   for n in vlens)
+        result["prefill_varlen"] = {
+            "workload": "qwen32k-varlen: B4 prompts of 32768, 24576, 16384, 8192 tokens padded to 32768, "
+                        "Hq40 Hkv8 D128 bf16, sink keys x3, S4 R1020 W128; prefill+LSE+lazy ratio",
+            "ms": round(v_ms, 4), "tflops": round(v_fl / v_ms / 1e9, 2),
+            "frac_mfma_peak": round(v_fl / v_ms / 1e9 * 1e12 / PEAK_BF16, 4), "flop": v_fl}
+        log(f"varlen prefill: {v_ms:.3f} ms, {v_fl / v_ms / 1e9:.1f} TFLOP/s")
+        del vq, vk, vv, vout, vlse, vrows, vratio
+        torch.cuda.empty_cache()
+
     # hybrid decode step: B8, context 100000, 64 layers (32 full + 32 streaming)
     if not args.no_decode:
         dw = synth.DECODE100K
@@ -271,7 +298,45 @@ def main() -> int:
                             "ms_per_step": round(d_ms, 4), "gbps": round(gbps, 1),
                             "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
                             "bytes_per_step": bytes_step}
-        del graph, qs, ks_, vs_, outs, lses, ws
+        del graph
+        # The same step with eight different contexts on the full layers.
+        if not args.no_varlen:
+            dlens = synth.DECODE100K_VARLEN_LENS
+            full_lens = torch.tensor(dlens, device=dev, dtype=torch.int32)
+            stream_lens = torch.tensor([min(n, lens[-1]) for n in dlens], device=dev, dtype=torch.int32)
+            vbytes = sum(sum(2 * dw.Hkv * min(n, lens[l]) * dw.D * 2 for n in dlens) + 2 * dw.B * dw.Hq * dw.D * 2
+                         for l in range(L))
+
+            def decode_all_varlen(st):
+                for l in range(L):
+                    api.lt_hybrid_decode_attn_varlen(qs[l], ks_[l], vs_[l], full_lens if l < nfull else stream_lens,
+                                                     lens[l], outs[l], lses[l], ws, 0.0, st)
+
+            with torch.cuda.stream(cap):
+                decode_all_varlen(cap)
+            torch.cuda.synchronize()
+            vgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(vgraph, stream=cap):
+                decode_all_varlen(cap)
+            torch.cuda.synchronize()
+            for _ in range(Wm):
+                vgraph.replay()
+            torch.cuda.synchronize()
+            a.record(stream)
+            for _ in range(K):
+                vgraph.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            vd_ms = a.elapsed_time(b) / K
+            vgbps = vbytes / (vd_ms * 1e-3) / 1e9
+            log(f"varlen decode: {vd_ms:.3f} ms/step, {vgbps:.1f} GB/s")
+            result["decode_varlen"] = {
+                "workload": "decode100k-varlen: the decode100k step with contexts 100000, 87500, ..., 12500 "
+                            "on the full layers (per-sequence lengths on the device), 1024 on the streaming ones",
+                "ms_per_step": round(vd_ms, 4), "gbps": round(vgbps, 1),
+                "frac_hbm_peak": round(vgbps * 1e9 / PEAK_HBM, 4), "bytes_per_step": vbytes}
+            del vgraph
+        del qs, ks_, vs_, outs, lses, ws
         torch.cuda.empty_cache()
 
     # Measured peaks: the matrix-core and HBM-read rates the chip delivers in

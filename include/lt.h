@@ -92,8 +92,8 @@ typedef struct {
  *     queries i = N-W..N-1, r_i = sum over keys j <= i with j < S or
  *     j > i-R of exp(s_ij - lse_i); lazy_ratio [B,Hq] fp32 receives the mean
  *     of the W values, summed in row order.  Both required.  The numerator is
- *     taken after the main pass from the sink and recent key tiles only; the
- *     denominator is the LSE just produced.
+ *     summed in the main pass, on the sink and recent key steps of the
+ *     observed rows only, next to the softmax sum that gives the LSE.
  *   Needs S >= 0, R >= 1.  bf16 runs on the matrix cores (fp32 accumulate,
  *   softmax weights rounded to bf16 for the P.V product); f32 runs in fp32.
  */
@@ -159,6 +159,64 @@ int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt
 int lt_stream_cache_append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
                            int B, int Hkv, int D, int dtype, int S, int R, int64_t pos,
                            hipStream_t stream);
+
+/*
+ * Variable-length batches (padded layout).  Sequence b of a batch has its
+ * own length, given per sequence in a DEVICE int32 array of B entries (so
+ * that a captured HIP graph can be replayed with new lengths); its rows are
+ * positions [0, len_b) of the padded tensors, and every method step runs on
+ * each sequence as if it were alone: causal from its own position 0, its own
+ * last W queries observed, its own sink + recent slice.  Lengths are read on
+ * the device and cannot be checked there: a value below 0 counts as 0, one
+ * above the padded size as the padded size.  Rows at or past len_b are
+ * neither read (q, k, v) nor written (out, lse) -- their contents are left
+ * as they were.  Everything else (views, validation, errors) is as in the
+ * call without _varlen; a NULL length array is LT_ERR_NULL.
+ *
+ * Prefill: seq_lens [B]; shape->N is the padded length.  lse keeps its
+ * [B,Hq,N] layout.  Lazy ratio: a sequence observes its last min(W, len_b)
+ * queries; lazy_rows[b,h,k] holds row len_b - W + k, the W - len_b slots of
+ * rows before position 0 (len_b < W) are set to NaN, and lazy_ratio is the
+ * mean of the observed rows (NaN for an empty sequence).
+ */
+int lt_prefill_attn_lse_lazy_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q,
+                                    lt_view k, lt_view v, lt_view out, float *lse, int S, int R,
+                                    int W, float *lazy_rows, float *lazy_ratio, hipStream_t stream);
+
+/* Streaming attention over a padded variable-length batch (seq_lens [B]). */
+int lt_streaming_attn_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
+                             lt_view v, lt_view out, float *lse, int S, int R, hipStream_t stream);
+
+/*
+ * Decode over caches of different lengths: sequence b attends to rows
+ * [0, kv_lens[b]) of its cache.  max_kv_len bounds every kv_lens[b] and sizes
+ * the workspace (lt_hybrid_decode_workspace_bytes with kv_len = max_kv_len).
+ * kv_lens[b] == 0 gives out = 0 and lse = -inf for that sequence.
+ */
+int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float scale,
+                                 const void *q, lt_view k_cache, lt_view v_cache,
+                                 const int32_t *kv_lens, int64_t max_kv_len, void *out, float *lse,
+                                 void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Compaction of a padded variable-length batch: sequence b keeps positions
+ * [0,S) and [len_b-R, len_b) of its own length, in the ring slot order of
+ * lt_compact_kv_streaming (every row in order when len_b <= S+R); slots at or
+ * past min(len_b, S+R) are left untouched.
+ */
+int lt_compact_kv_streaming_varlen(lt_view k_full, lt_view v_full, lt_view k_stream,
+                                   lt_view v_stream, int B, int Hkv, int N, int D, int dtype, int S,
+                                   int R, const int32_t *seq_lens, hipStream_t stream);
+
+/*
+ * Decode-time append with each sequence at its own position: pos [B] device
+ * int32; sequence b's new rows go to the slot of pos[b] (same rule as
+ * lt_stream_cache_append); a negative pos[b] writes nothing for b.  The
+ * caches must hold S+R slots.
+ */
+int lt_stream_cache_append_varlen(lt_view k_stream, lt_view v_stream, const void *k_new,
+                                  const void *v_new, int B, int Hkv, int D, int dtype, int S, int R,
+                                  const int32_t *pos, hipStream_t stream);
 
 /*
  * (full, streaming) KV bytes of one layer: 2*B*Hkv*N*D*e and

@@ -146,6 +146,104 @@ def lt_stream_cache_append(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new
                                        int(pos), _stream(stream)))
 
 
+def _lens(t: torch.Tensor, B: int, name: str) -> int:
+    """Per-sequence length / position array: a contiguous int32 [B] device tensor."""
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != B or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name} must be a contiguous int32 [B] device tensor")
+    return t.data_ptr()
+
+
+def lt_prefill_attn_lse_lazy_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                    lse: torch.Tensor, seq_lens: torch.Tensor, S: int, R: int, W: int,
+                                    lazy_rows: Optional[torch.Tensor] = None,
+                                    lazy_ratio: Optional[torch.Tensor] = None, scale: float = 0.0,
+                                    stream=None) -> None:
+    """Padded variable-length batch: q [B,Hq,N,D] etc. padded to N; seq_lens
+    [B] int32 on the device."""
+    _same_dtype(q, k, v, out)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, out")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    shp = _shape(q, k, scale)
+    check(lib().lt_prefill_attn_lse_lazy_varlen(ctypes.byref(shp), _lens(seq_lens, q.shape[0], "seq_lens"),
+                                                _view(q), _view(k), _view(v), _view(out), _ptr(lse), S, R,
+                                                W, _ptr(lazy_rows), _ptr(lazy_ratio), _stream(stream)))
+
+
+def lt_streaming_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                             lse: Optional[torch.Tensor], seq_lens: torch.Tensor, S: int, R: int,
+                             scale: float = 0.0, stream=None) -> None:
+    _same_dtype(q, k, v, out)
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, out")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    shp = _shape(q, k, scale)
+    check(lib().lt_streaming_attn_varlen(ctypes.byref(shp), _lens(seq_lens, q.shape[0], "seq_lens"), _view(q),
+                                         _view(k), _view(v), _view(out), _ptr(lse), S, R, _stream(stream)))
+
+
+def lt_hybrid_decode_attn_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                 kv_lens: torch.Tensor, max_kv_len: int, out: torch.Tensor,
+                                 lse: Optional[torch.Tensor], ws: torch.Tensor, scale: float = 0.0,
+                                 stream=None) -> None:
+    """kv_lens [B] int32 on the device, each <= max_kv_len; ws sized by
+    lt_hybrid_decode_workspace_bytes(..., max_kv_len)."""
+    if not (q.is_contiguous() and out.is_contiguous() and ws.is_contiguous()):
+        raise ValueError("q, out and ws must be contiguous")
+    _same_dtype(q, k_cache, v_cache, out)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or k_cache.shape[0] != B or k_cache.shape[3] != D \
+            or k_cache.shape[2] < max_kv_len or v_cache.shape[:2] != k_cache.shape[:2] \
+            or v_cache.shape[2] < max_kv_len or v_cache.shape[3] != D:
+        raise ValueError("decode shape mismatch")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    check(lib().lt_hybrid_decode_attn_varlen(B, Hq, k_cache.shape[1], D, _dtype_code(q), float(scale),
+                                             q.data_ptr(), _view(k_cache), _view(v_cache),
+                                             _lens(kv_lens, B, "kv_lens"), int(max_kv_len), out.data_ptr(),
+                                             _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                             _stream(stream)))
+
+
+def lt_compact_kv_streaming_varlen(k_full: torch.Tensor, v_full: torch.Tensor, k_stream: torch.Tensor,
+                                   v_stream: torch.Tensor, seq_lens: torch.Tensor, S: int, R: int,
+                                   stream=None) -> None:
+    B, Hkv, N, D = k_full.shape
+    rows = min(N, S + R)
+    if v_full.shape != k_full.shape:
+        raise ValueError("k_full / v_full shape mismatch")
+    for t in (k_stream, v_stream):
+        if t.shape[0] != B or t.shape[1] != Hkv or t.shape[2] < rows or t.shape[3] != D:
+            raise ValueError("streaming cache too small")
+    _same_dtype(k_full, v_full, k_stream, v_stream)
+    check(lib().lt_compact_kv_streaming_varlen(_view(k_full), _view(v_full), _view(k_stream),
+                                               _view(v_stream), B, Hkv, N, D, _dtype_code(k_full), S, R,
+                                               _lens(seq_lens, B, "seq_lens"), _stream(stream)))
+
+
+def lt_stream_cache_append_varlen(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, S: int, R: int, pos: torch.Tensor,
+                                  stream=None) -> None:
+    """pos [B] int32 on the device (negative: skip that sequence); the caches
+    hold S + R slots."""
+    B, Hkv, rows, D = k_stream.shape
+    if not (k_new.is_contiguous() and v_new.is_contiguous()):
+        raise ValueError("k_new and v_new must be contiguous")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) \
+            or v_stream.shape != k_stream.shape:
+        raise ValueError("append shape mismatch")
+    if rows < S + R:
+        raise ValueError("the streaming cache needs S + R slots")
+    _same_dtype(k_stream, v_stream, k_new, v_new)
+    check(lib().lt_stream_cache_append_varlen(_view(k_stream), _view(v_stream), k_new.data_ptr(),
+                                              v_new.data_ptr(), B, Hkv, D, _dtype_code(k_stream), S, R,
+                                              _lens(pos, B, "pos"), _stream(stream)))
+
+
 def lt_kv_bytes(B: int, Hkv: int, N: int, D: int, dtype: int, S: int, R: int) -> Tuple[int, int]:
     full, stream = ctypes.c_int64(), ctypes.c_int64()
     check(lib().lt_kv_bytes(B, Hkv, N, D, dtype, S, R, ctypes.byref(full), ctypes.byref(stream)))

@@ -26,10 +26,13 @@
 //   running sum stays per lane and is reduced once at the end.  Scores are
 //   kept in log2 units (scale*log2 e folded into one fma before exp2).
 //
-// Launch order: blockIdx.x % U picks the (batch, KV head) unit so that with
-// B*Hkv a multiple of 8 each XCD (dispatch is round-robin over the 8 XCDs)
-// keeps one KV head's K/V in its own L2; blockIdx.x / U walks the row tiles
-// longest-first to even out the causal triangle.
+// Launch order: sequence by sequence; within a sequence blockIdx.x % Hkv
+// picks the KV head, so that with Hkv a multiple of 8 each XCD (dispatch is
+// round-robin over the 8 XCDs) keeps one KV head's K/V in its own L2, and the
+// row tiles run longest-first to even out the causal triangle.  Keeping one
+// sequence's workgroups together keeps its K/V in the shared caches; with
+// sequences of different lengths, interleaving them (most of the first
+// workgroups then exit at once) ran at half the rate.
 
 #include <type_traits>
 
@@ -177,13 +180,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // every per-wave test below is a scalar branch, not an exec-mask one.
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int U = a.B * a.Hkv;
-    const int unit = (int)(blockIdx.x % U);
-    const int qt = a.n_qtiles - 1 - (int)(blockIdx.x / U);
-    const int hk = unit % a.Hkv, b = unit / a.Hkv;
-    const int N = a.N, G = a.G;
+    const int per_b = a.n_qtiles * a.Hkv;
+    const int b = (int)(blockIdx.x / per_b);
+    const int rem = (int)(blockIdx.x % per_b);
+    const int hk = rem % a.Hkv;
+    const int qt = a.n_qtiles - 1 - rem / a.Hkv;
+    const int N = seq_length(a.seq_len, b, a.N), G = a.G;
     const float c = a.c;
     const int r0 = qt * BROWS;
+    if (r0 >= N * G) return;  // past this sequence's end (whole workgroup, before any barrier)
     const int rw0 = r0 + wave * WROWS;
     const int nrows = N * G;
     const int wg_last = ((r0 + BROWS < nrows ? r0 + BROWS : nrows) - 1) / G;  // last position
@@ -510,7 +515,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 *(bf16x4 *)(op + db * 16) = w;
             }
             if (a.lse != nullptr && g == 0)
-                a.lse[((int64_t)b * a.Hq + head[rb]) * N + pos[rb]] = (m[rb] + __log2f(lt)) * kLn2;
+                a.lse[((int64_t)b * a.Hq + head[rb]) * a.N + pos[rb]] = (m[rb] + __log2f(lt)) * kLn2;
         }
         if (LAZY) {
             const float zt = group_sum(lz[rb]);
@@ -520,14 +525,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
 }
 
-// Per-head lazy ratio: mean of the W per-row values, summed in row order.
-__global__ void lazy_reduce_kernel(const float *rows, float *ratio, int BH, int W) {
+// Per-head lazy ratio: mean of the observed rows, summed in row order.  A
+// sequence observes its last min(W, n) rows; slot k holds row n - W + k, so
+// the slots of rows before position 0 (n < W) are set to NaN.
+__global__ void lazy_reduce_kernel(float *rows, float *ratio, int BH, int W, const int *seq_len, int Hq,
+                                   int N) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= BH) return;
-    const float *r = rows + (int64_t)i * W;
+    const int n = seq_length(seq_len, i / Hq, N);
+    const int cnt = n < W ? n : W;
+    float *r = rows + (int64_t)i * W;
+    for (int w = 0; w < W - cnt; ++w) r[w] = __builtin_nanf("");
     float acc = 0.f;
-    for (int w = 0; w < W; ++w) acc += r[w];
-    ratio[i] = acc / (float)W;
+    for (int w = W - cnt; w < W; ++w) acc += r[w];
+    ratio[i] = cnt > 0 ? acc / (float)cnt : __builtin_nanf("");
 }
 
 // MODES: bit mask of the modes this configuration is built for.
@@ -577,10 +588,10 @@ hipError_t launch_attn_bf16(const AttnArgs &a, int D, int mode, hipStream_t st) 
     return launch_d<128>(a, mode, st);
 }
 
-hipError_t launch_lazy_reduce(const float *lazy_rows, float *lazy_ratio, int BH, int W,
-                              hipStream_t st) {
+hipError_t launch_lazy_reduce(float *lazy_rows, float *lazy_ratio, int BH, int W, const int *seq_len,
+                              int Hq, int N, hipStream_t st) {
     hipLaunchKernelGGL(lazy_reduce_kernel, dim3((BH + 255) / 256), dim3(256), 0, st, lazy_rows,
-                       lazy_ratio, BH, W);
+                       lazy_ratio, BH, W, seq_len, Hq, N);
     return hipGetLastError();
 }
 

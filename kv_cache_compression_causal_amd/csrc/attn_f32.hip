@@ -32,8 +32,9 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
     const int row = lane % ROWS, half = lane / ROWS;
     const int bh = blockIdx.y;
     const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
-    const int N = a.N;
+    const int N = seq_length(a.seq_len, b, a.N);
     const int q0 = blockIdx.x * ROWS;
+    if (q0 >= N) return;  // past this sequence's end (whole block, before any barrier)
     const int i = q0 + row;
     const bool row_ok = i < N;
     const float c = a.c;
@@ -128,7 +129,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         for (int d = 0; d < 64; d += 4)
             *(float4 *)(op + d) = make_float4(o[d] * inv, o[d + 1] * inv, o[d + 2] * inv,
                                               o[d + 3] * inv);
-        if (a.lse != nullptr && half == 0) a.lse[((int64_t)b * a.Hq + h) * N + i] = lse2 * kLn2;
+        if (a.lse != nullptr && half == 0) a.lse[((int64_t)b * a.Hq + h) * a.N + i] = lse2 * kLn2;
     }
 
     // Lazy-ratio epilogue: sum exp2(s_ij*c - lse2_i) over the sink keys and

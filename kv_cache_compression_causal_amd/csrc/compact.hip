@@ -17,7 +17,6 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
     const int chunks_per_row = row_bytes / 16;
     const int64_t per_head = (int64_t)a.rows_out * chunks_per_row;
     const int64_t total = (int64_t)a.B * a.Hkv * per_head * 2;
-    const bool all_rows = a.N <= a.S + a.R;
     for (int64_t idx = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; idx < total;
          idx += (int64_t)gridDim.x * blockDim.x) {
         const int which = (int)(idx / (total / 2));  // 0 = K, 1 = V
@@ -27,10 +26,13 @@ __global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
         const int r = (int)(rem / chunks_per_row);
         const int ch = (int)(rem % chunks_per_row);
         const int b = bh / a.Hkv, h = bh % a.Hkv;
+        // this sequence's length: rows_out = min(n, S + R) rows are kept
+        const int n = seq_length(a.seq_len, b, a.N);
+        if (r >= (n < a.S + a.R ? n : a.S + a.R)) continue;
         int src_row = r;
-        if (!all_rows && r >= a.S) {
-            // the recent position p in [N-R, N) whose ring slot is r
-            const int base = a.N - a.R;
+        if (n > a.S + a.R && r >= a.S) {
+            // the recent position p in [n-R, n) whose ring slot is r
+            const int base = n - a.R;
             int m = (r - base) % a.R;
             if (m < 0) m += a.R;
             src_row = base + m;
@@ -59,10 +61,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
         const int64_t rem = idx % (total / 2);
         const int bh = (int)(rem / chunks_per_row), ch = (int)(rem % chunks_per_row);
         const int b = bh / a.Hkv, h = bh % a.Hkv;
+        int64_t slot = a.slot;
+        if (a.pos != nullptr) {  // this sequence's own position and its ring slot
+            const int p = a.pos[b];
+            if (p < 0) continue;
+            slot = p < a.S ? p : a.S + (p - a.S) % a.R;
+        }
         const char *src = (const char *)(which == 0 ? a.kn : a.vn) + ((int64_t)bh * a.D) * a.elem;
         char *dst = which == 0
-                        ? (char *)a.ks + ((int64_t)b * a.ks_sb + (int64_t)h * a.ks_sh + a.slot * a.ks_sn) * a.elem
-                        : (char *)a.vs + ((int64_t)b * a.vs_sb + (int64_t)h * a.vs_sh + a.slot * a.vs_sn) * a.elem;
+                        ? (char *)a.ks + ((int64_t)b * a.ks_sb + (int64_t)h * a.ks_sh + slot * a.ks_sn) * a.elem
+                        : (char *)a.vs + ((int64_t)b * a.vs_sb + (int64_t)h * a.vs_sh + slot * a.vs_sn) * a.elem;
         *(uint4 *)(dst + ch * 16) = *(const uint4 *)(src + ch * 16);
     }
 }

@@ -3,10 +3,16 @@
 // paragraph; press-release page, results) is what this step reads, so it is
 // bound by HBM bandwidth.
 //
-// Split-KV: workgroup (split, b*Hkv + kv head) streams keys
-// [split*kps, (split+1)*kps) once and serves all G query heads of the group
-// from each K/V row, keeping one online-softmax state per head.  A second
-// kernel merges the per-split states with their log-sum-exps.
+// Split-KV over equal parts of the batch: for each KV head the contexts of
+// the B sequences are laid end to end (T keys in all) and cut into P parts
+// of Q = ceil(T/P) keys.  Workgroup (kv head, part) streams its part once --
+// a segment of one sequence, or the end of one and the start of the next --
+// and serves all G query heads of the group from each K/V row, keeping one
+// online-softmax state per head and writing one partial state per segment.
+// Every workgroup gets the same number of keys whatever the per-sequence
+// lengths are.  A second kernel merges each sequence's partial states with
+// their log-sum-exps.  The lengths may live on the device (kv_lens), so the
+// partition is computed there, by every workgroup, from them.
 //
 // bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16 for Q.K and P.V):
 //   S^T (16 keys x 16 columns) = K Q^T, where column c < G is query head
@@ -51,9 +57,103 @@ __device__ __forceinline__ float group_max(float x) {
     return fmaxf(__builtin_bit_cast(float, a1), __builtin_bit_cast(float, b1));
 }
 
-// Partial state layout: ws[(bh * n_splits + split) * (D + 2) + {0..D-1: o/l, D: m (log2), D+1: l}]
+// Makes a uniform value available at this point: the kernel-argument reads
+// the decode kernel needs are all placed at its entry this way, so they are
+// issued together instead of in dependent rounds after the partition's
+// branches (each round trip to argument memory is microseconds that a short
+// layer pays in full).
+template <typename T>
+__device__ __forceinline__ void read_now(const T &x) {
+    asm volatile("" ::"s"(x));
+}
+
+// Context length of sequence b (the uniform kv_len, or kv_lens[b] clamped
+// to [0, kv_len]); uniform across the workgroup.
+__device__ __forceinline__ int64_t ctx_len(const DecodeArgs &a, int b) {
+    if (a.kv_lens == nullptr) return a.kv_len;
+    const int x = __builtin_amdgcn_readfirstlane(a.kv_lens[b]);
+    return x < 0 ? 0 : (x > a.kv_len ? a.kv_len : (int64_t)x);
+}
+
+// x / y for x >= 0, y > 0 (uniform values).  A 64-bit division expands to
+// hundreds of vector instructions, which a short layer's workgroups would
+// wait on before their first load; 32-bit operands (every realistic size)
+// take the short path.
+__device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
+    // The hardware has no scalar divide: the quotient comes out of vector
+    // registers and is moved back to a scalar one, so that nothing derived
+    // from it occupies vector registers (they decide the occupancy).
+    if (((x | y) >> 31) == 0) return (int64_t)__builtin_amdgcn_readfirstlane((uint32_t)x / (uint32_t)y);
+    const int64_t q = x / y;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)q);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(q >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Total keys T of one head over the batch and the part size Q = ceil(T/P)
+// (given by the host when every context has the same length).
+struct Partition {
+    int64_t T, Q;
+};
+__device__ __forceinline__ Partition partition(const DecodeArgs &a) {
+    if (a.kv_lens == nullptr) return Partition{(int64_t)a.B * a.kv_len, a.part_keys};
+    int64_t T = 0;
+    for (int b = 0; b < a.B; ++b) T += ctx_len(a, b);
+    return Partition{T, T > 0 ? div_nonneg(T + a.n_parts - 1, a.n_parts) : 0};
+}
+
+// First key of sequence b in the end-to-end order.
+__device__ __forceinline__ int64_t ctx_start(const DecodeArgs &a, int b) {
+    if (a.kv_lens == nullptr) return (int64_t)b * a.kv_len;
+    int64_t S = 0;
+    for (int i = 0; i < b; ++i) S += ctx_len(a, i);
+    return S;
+}
+
+// Calls f(b, kbeg, kend, slot) for every sequence b that part `part`
+// overlaps, with its keys [kbeg, kend) in that part.  The partial of
+// (sequence b, part p) goes to workspace slot p + b: slots increase with
+// (b, p) in order and a sequence's parts are consecutive, so no two pairs
+// share a slot and P + B - 1 slots suffice.  The first segment is called
+// outside the loop: as straight-line code its loads issue right after the
+// partition arithmetic (inside a loop the compiler hoisted the invariant
+// setup of every segment in front of them, which short layers paid for).
+template <typename F>
+__device__ __forceinline__ void for_each_segment(const DecodeArgs &a, int part, F &&f) {
+    const Partition pt = partition(a);
+    if (pt.T == 0) return;
+    const int64_t g0 = (int64_t)part * pt.Q;
+    if (g0 >= pt.T) return;
+    const int64_t g1 = g0 + pt.Q < pt.T ? g0 + pt.Q : pt.T;
+    // The sequence holding key g0.
+    int b;
+    int64_t S, n;
+    if (a.kv_lens == nullptr) {
+        b = (int)div_nonneg(g0, a.kv_len);
+        S = (int64_t)b * a.kv_len;
+        n = a.kv_len;
+    } else {
+        b = 0;
+        S = 0;
+        n = ctx_len(a, 0);
+        while (b + 1 < a.B && S + n <= g0) {
+            S += n;
+            n = ctx_len(a, ++b);
+        }
+    }
+    f(b, g0 - S, (g1 < S + n ? g1 : S + n) - S, part + b);
+    // Sequences after it that the part still reaches.
+    for (S += n, ++b; b < a.B && S < g1; ++b) {
+        n = ctx_len(a, b);
+        if (n > 0) f(b, (int64_t)0, (g1 < S + n ? g1 : S + n) - S, part + b);
+        S += n;
+    }
+}
+
+// Partial state of (slot, query head h):
+// ws[(slot * Hq + h) * (D + 2) + {0..D-1: o/l, D: m (log2), D+1: l}]
 //
-// Each wave streams its own 32-key steps of the split (steps w, w+4, ...):
+// Each wave streams its own 32-key steps of a segment (steps w, w+4, ...):
 // K goes straight from global memory into the matrix-core A operand (lane
 // (c, g) holds dims (D/4)g .. (D/4)(g+1)-1 of key c of a 16-key block,
 // contiguous bytes), one step ahead in registers.  V rows are loaded one step
@@ -62,9 +162,9 @@ __device__ __forceinline__ float group_max(float x) {
 // transposed.  All loads are plain register loads, so the compiler's
 // load-counter waits stay exact (mixing in direct global->LDS loads made it
 // wait for every outstanding load).  No workgroup barrier until the four
-// waves merge their states at the end.
+// waves merge their states at the end of the segment.
 template <int D>
-__global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;       // 32-dim steps (Q.K)
     constexpr int DB = D / 16;       // 16-dim blocks (O)
     constexpr int STEP = 32;         // keys per step
@@ -84,50 +184,55 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
     // scalar branches and the load counters are tracked exactly across them.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int split = blockIdx.x;
-    const int bhk = blockIdx.y;
-    const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+    const int hk = blockIdx.x;    // KV heads fastest: with 8 of them each XCD streams one
+    const int part = blockIdx.y;
+    read_now(a.q), read_now(a.k), read_now(a.v), read_now(a.ws);
+    read_now(a.k_sb), read_now(a.k_sh), read_now(a.k_sn);
+    read_now(a.v_sb), read_now(a.v_sh), read_now(a.v_sn);
+    read_now(a.B), read_now(a.Hq), read_now(a.G), read_now(a.c);
+    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts);
     const int G = a.G;
-    const int64_t kbeg = (int64_t)split * a.keys_per_split;
-    const int64_t kend = kbeg + a.keys_per_split < a.kv_len ? kbeg + a.keys_per_split : a.kv_len;
-    const int nsteps = (int)((kend - kbeg + STEP - 1) / STEP);
     const float c = a.c;
     bf16 *const slot = (bf16 *)smem + wave * VTILE;
 
-    const bf16 *kbase = (const bf16 *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
-    const bf16 *vbase = (const bf16 *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
+    // One segment: keys [kbeg, kend) of sequence b; the merged state of the
+    // four waves goes to workspace slot ws_slot.
+    auto segment = [&](int b, int64_t kbeg, int64_t kend, int ws_slot) {
+        const int nsteps = (int)((kend - kbeg + STEP - 1) / STEP);
+        const bf16 *kbase = (const bf16 *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
+        const bf16 *vbase = (const bf16 *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
 
-    // Q^T: lane holds column c16 (query head hk*G + c16, zero if c16 >= G),
-    // dims (D/4)g + 8ks .. +7 of step ks -- the same dim order as the K operand.
-    bf16x8 qreg[KS];
-    {
-        const bool col_ok = c16 < G;
-        const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + (col_ok ? c16 : 0)) * D + (D / 4) * g;
+        // Q^T: lane holds column c16 (query head hk*G + c16, zero if c16 >= G),
+        // dims (D/4)g + 8ks .. +7 of step ks -- the same dim order as the K operand.
+        bf16x8 qreg[KS];
+        {
+            const bool col_ok = c16 < G;
+            const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + (col_ok ? c16 : 0)) * D + (D / 4) * g;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            bf16x8 v = *(const bf16x8 *)(qp + 8 * ks);
-            qreg[ks] = col_ok ? v : bf16x8{};
+            for (int ks = 0; ks < KS; ++ks) {
+                bf16x8 v = *(const bf16x8 *)(qp + 8 * ks);
+                qreg[ks] = col_ok ? v : bf16x8{};
+            }
         }
-    }
 
-    bf16x8 kreg[2][2][KPL];  // [buffer][16-key block][load]
-    bf16x8 vreg[NVL];        // V rows of the next step: row RPI*u + lane/CPR, chunk lane%CPR
-    auto issue = [&](int t, int buf) {
-        const int64_t key0 = kbeg + (int64_t)t * STEP;
+        bf16x8 kreg[2][2][KPL];  // [buffer][16-key block][load]
+        bf16x8 vreg[NVL];        // V rows of the next step: row RPI*u + lane/CPR, chunk lane%CPR
+        auto issue = [&](int t, int buf) {
+            const int64_t key0 = kbeg + (int64_t)t * STEP;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            int64_t key = key0 + kb * 16 + c16;
-            key = key < kend ? key : kend - 1;
-            const bf16 *kp = kbase + key * a.k_sn + (D / 4) * g;
+            for (int kb = 0; kb < 2; ++kb) {
+                int64_t key = key0 + kb * 16 + c16;
+                key = key < kend ? key : kend - 1;
+                const bf16 *kp = kbase + key * a.k_sn + (D / 4) * g;
 #pragma unroll
-            for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
-        }
+                for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
+            }
 #pragma unroll
-        for (int u = 0; u < NVL; ++u) {
-            int64_t key = key0 + RPI * u + lane / CPR;
-            key = key < kend ? key : kend - 1;
-            vreg[u] = *(const bf16x8 *)(vbase + key * a.v_sn + (lane % CPR) * 8);
-        }
+            for (int u = 0; u < NVL; ++u) {
+                int64_t key = key0 + RPI * u + lane / CPR;
+                key = key < kend ? key : kend - 1;
+                vreg[u] = *(const bf16x8 *)(vbase + key * a.v_sn + (lane % CPR) * 8);
+            }
     };
     // Write the staged V rows into the wave's slot, each 16-byte chunk at
     // its swizzled place.
@@ -251,56 +356,59 @@ __global__ __launch_bounds__(256) void decode_bf16_kernel(DecodeArgs a) {
             L += f * red_l[w][col];
             O += f * red_o[w][col][d];
         }
-        float *dst = a.ws + (((int64_t)b * a.Hq + hk * G + col) * a.n_splits + split) * (D + 2);
+        float *dst = a.ws + ((int64_t)ws_slot * a.Hq + hk * G + col) * (D + 2);
         dst[d] = O / L;
         if (d == 0) {
             dst[D] = M;
             dst[D + 1] = L;
         }
     }
+    __syncthreads();  // the merge buffers share LDS with the next segment's V slots
+    };
+    for_each_segment(a, part, segment);
 }
 
-// fp32: block of 64 lanes per (split, b*Hq + h); lane owns dims lane, lane+64.
+// fp32: block of 64 lanes per (query head, part), looping over the part's
+// segments; lane owns dims lane, lane+64.
 template <int D>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
-    const int split = blockIdx.x;
-    const int bh = blockIdx.y;
-    const int b = bh / a.Hq, h = bh % a.Hq, hk = h / a.G;
-    const int64_t kbeg = (int64_t)split * a.keys_per_split;
-    const int64_t kend = kbeg + a.keys_per_split < a.kv_len ? kbeg + a.keys_per_split : a.kv_len;
-    const float *kbase = (const float *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
-    const float *vbase = (const float *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
-    float q[PER], o[PER];
+    const int h = blockIdx.x, hk = h / a.G;
+    const int part = blockIdx.y;
+    for_each_segment(a, part, [&](int b, int64_t kbeg, int64_t kend, int ws_slot) {
+        const float *kbase = (const float *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
+        const float *vbase = (const float *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
+        float q[PER], o[PER];
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-        q[u] = ((const float *)a.q)[(int64_t)bh * D + lane + 64 * u];
-        o[u] = 0.f;
-    }
-    float m = kNegInf, l = 0.f;
-    for (int64_t j = kbeg; j < kend; ++j) {
-        float part = 0.f;
+        for (int u = 0; u < PER; ++u) {
+            q[u] = ((const float *)a.q)[((int64_t)b * a.Hq + h) * D + lane + 64 * u];
+            o[u] = 0.f;
+        }
+        float m = kNegInf, l = 0.f;
+        for (int64_t j = kbeg; j < kend; ++j) {
+            float dot = 0.f;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) part = __builtin_fmaf(q[u], kbase[j * a.k_sn + lane + 64 * u], part);
+            for (int u = 0; u < PER; ++u) dot = __builtin_fmaf(q[u], kbase[j * a.k_sn + lane + 64 * u], dot);
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-        const float s = part * a.c;
-        const float mnew = fmaxf(m, s);
-        const float alpha = exp2f(m - mnew);
-        const float p = exp2f(s - mnew);
-        m = mnew;
-        l = l * alpha + p;
+            for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
+            const float s = dot * a.c;
+            const float mnew = fmaxf(m, s);
+            const float alpha = exp2f(m - mnew);
+            const float p = exp2f(s - mnew);
+            m = mnew;
+            l = l * alpha + p;
 #pragma unroll
-        for (int u = 0; u < PER; ++u) o[u] = __builtin_fmaf(p, vbase[j * a.v_sn + lane + 64 * u], o[u] * alpha);
-    }
-    float *dst = a.ws + ((int64_t)bh * a.n_splits + split) * (D + 2);
+            for (int u = 0; u < PER; ++u) o[u] = __builtin_fmaf(p, vbase[j * a.v_sn + lane + 64 * u], o[u] * alpha);
+        }
+        float *dst = a.ws + ((int64_t)ws_slot * a.Hq + h) * (D + 2);
 #pragma unroll
-    for (int u = 0; u < PER; ++u) dst[lane + 64 * u] = o[u] / l;
-    if (lane == 0) {
-        dst[D] = m;
-        dst[D + 1] = l;
-    }
+        for (int u = 0; u < PER; ++u) dst[lane + 64 * u] = o[u] / l;
+        if (lane == 0) {
+            dst[D] = m;
+            dst[D + 1] = l;
+        }
+    });
 }
 
 // Merge split partials: out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M);
@@ -312,63 +420,72 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 template <int D, typename T>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     constexpr int CH = 16;
+    read_now(a.ws), read_now(a.o), read_now(a.lse), read_now(a.B), read_now(a.Hq);
+    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts);
     const int bh = blockIdx.x;
+    const int b = bh / a.Hq, h = bh % a.Hq;
     const int d = threadIdx.x;
-    const int n = a.n_splits;
-    const float *src = a.ws + (int64_t)bh * n * (D + 2);
+    // Sequence b's partial states: the parts p0..p1 its context overlaps, in
+    // slots p0 + b .. p1 + b (none for an empty context).
+    const Partition pt = partition(a);
+    const int64_t S = ctx_start(a, b), len = ctx_len(a, b);
+    const int64_t p0 = len > 0 ? div_nonneg(S, pt.Q) : 0;
+    const int n = len > 0 ? (int)(div_nonneg(S + len - 1, pt.Q) - p0) + 1 : 0;
+    const int64_t stride = (int64_t)a.Hq * (D + 2);
+    const float *src = a.ws + (p0 + b) * stride + (int64_t)h * (D + 2);
     float M = kNegInf, L = 0.f, O = 0.f;
     for (int s0 = 0; s0 < n; s0 += CH) {
         float mv[CH], lv[CH], ov[CH];
 #pragma unroll
         for (int i = 0; i < CH; ++i) {
             const int sp = s0 + i < n ? s0 + i : n - 1;
-            mv[i] = src[sp * (D + 2) + D];
-            lv[i] = src[sp * (D + 2) + D + 1];
-            ov[i] = src[sp * (D + 2) + d];
+            mv[i] = src[sp * stride + D];
+            lv[i] = src[sp * stride + D + 1];
+            ov[i] = src[sp * stride + d];
         }
         float Mc = M;
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             if (s0 + i < n) Mc = fmaxf(Mc, mv[i]);
-        const float f = __builtin_amdgcn_exp2f(M - Mc);  // 0 while M is -inf
+        // Splits without keys carry m = -inf, l = 0: they get weight 0 (and
+        // while every split so far is empty, M = Mc = -inf must not give NaN).
+        const float f = M == kNegInf ? 0.f : __builtin_amdgcn_exp2f(M - Mc);
         L *= f;
         O *= f;
 #pragma unroll
         for (int i = 0; i < CH; ++i)
             if (s0 + i < n) {
-                const float w = lv[i] * __builtin_amdgcn_exp2f(mv[i] - Mc);
+                const float w = mv[i] == kNegInf ? 0.f : lv[i] * __builtin_amdgcn_exp2f(mv[i] - Mc);
                 L += w;
                 O += w * ov[i];
             }
         M = Mc;
     }
-    ((T *)a.o)[(int64_t)bh * D + d] = (T)(O / L);
+    // An empty context (kv_lens[b] == 0): output 0, LSE -inf.
+    ((T *)a.o)[(int64_t)bh * D + d] = (T)(L > 0.f ? O / L : 0.f);
     if (d == 0 && a.lse != nullptr) a.lse[bh] = (M + log2f(L)) * kLn2;
 }
 
 }  // namespace
 
-int decode_num_splits(int B, int Hkv, int64_t kv_len) {
+int decode_num_parts(int B, int Hkv, int64_t kv_len) {
     // Aim for about 512 workgroups (two per CU, eight waves streaming their
-    // own steps) so enough loads are in flight to cover HBM latency; never
-    // fewer than one 64-key chunk per split.
-    const int64_t units = (int64_t)B * Hkv;
-    int64_t want = (512 + units - 1) / units;
-    const int64_t max_splits = (kv_len + kTile - 1) / kTile;
-    if (want > max_splits) want = max_splits;
+    // own steps) so enough loads are in flight to cover HBM latency; parts
+    // of at least kTile keys when every context has its full length.
+    int64_t want = (512 + Hkv - 1) / Hkv;
+    const int64_t max_parts = ((int64_t)B * kv_len + kTile - 1) / kTile;
+    if (want > max_parts) want = max_parts;
     if (want < 1) want = 1;
-    int64_t kps = (kv_len + want - 1) / want;
-    kps = (kps + kTile - 1) / kTile * kTile;
-    return (int)((kv_len + kps - 1) / kps);
+    return (int)want;
 }
 
-size_t decode_ws_bytes(int B, int Hq, int D, int n_splits) {
-    return (size_t)B * Hq * n_splits * (D + 2) * sizeof(float);
+size_t decode_ws_bytes(int B, int Hq, int D, int n_parts) {
+    return (size_t)(n_parts + B - 1) * Hq * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
     if (dtype == LT_BF16) {
-        dim3 grid((unsigned)a.n_splits, (unsigned)(a.B * a.Hkv));
+        dim3 grid((unsigned)a.Hkv, (unsigned)a.n_parts);
         if (a.D == 64) {
             hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(256), 0, st, a);
             hipLaunchKernelGGL((decode_combine_kernel<64, bf16>), dim3(a.B * a.Hq), dim3(64), 0, st, a);
@@ -377,7 +494,7 @@ hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
             hipLaunchKernelGGL((decode_combine_kernel<128, bf16>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
         }
     } else {
-        dim3 grid((unsigned)a.n_splits, (unsigned)(a.B * a.Hq));
+        dim3 grid((unsigned)a.Hq, (unsigned)a.n_parts);
         if (a.D == 64) {
             hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(64), 0, st, a);
             hipLaunchKernelGGL((decode_combine_kernel<64, float>), dim3(a.B * a.Hq), dim3(64), 0, st, a);

@@ -71,7 +71,127 @@ lt::AttnArgs make_args(const lt_shape *s, const lt_view &q, const lt_view &k, co
     a.scale = s->scale > 0.f ? s->scale : 1.f / sqrtf((float)s->D);
     a.c = a.scale * 1.4426950408889634f;
     a.S = S; a.R = R; a.W = W;
+    a.seq_len = nullptr;
     return a;
+}
+
+// The calls below with and without per-sequence lengths share these bodies;
+// `lens` is a device array of B lengths or nullptr.
+
+int prefill(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt_view v, lt_view out,
+            float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio, hipStream_t stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
+        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
+        return e;
+    if (lse == nullptr) return fail(LT_ERR_NULL, "lse is NULL");
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    if (W < 0 || W > shape->N) return fail(LT_ERR_SHAPE, "W %d outside [0, N=%d]", W, shape->N);
+    if (W > 0 && (lazy_rows == nullptr || lazy_ratio == nullptr))
+        return fail(LT_ERR_NULL, "W > 0 needs lazy_rows and lazy_ratio");
+    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, W, lazy_rows);
+    a.seq_len = lens;
+    const int mode = W > 0 ? lt::MODE_FULL_LAZY : lt::MODE_FULL;
+    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, mode, stream)
+                                            : lt::launch_attn_f32(a, shape->D, mode, stream);
+    if (he != hipSuccess) return hip_status(he, "prefill launch");
+    if (W > 0) {
+        he = lt::launch_lazy_reduce(lazy_rows, lazy_ratio, shape->B * shape->Hq, W, lens, shape->Hq, shape->N,
+                                    stream);
+        if (he != hipSuccess) return hip_status(he, "lazy reduce launch");
+    }
+    return ok();
+}
+
+int streaming(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt_view v, lt_view out,
+              float *lse, int S, int R, hipStream_t stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
+        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
+        return e;
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, 0, nullptr);
+    a.seq_len = lens;
+    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, lt::MODE_STREAM, stream)
+                                            : lt::launch_attn_f32(a, shape->D, lt::MODE_STREAM, stream);
+    if (he != hipSuccess) return hip_status(he, "streaming launch");
+    return ok();
+}
+
+int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q, lt_view k_cache,
+           lt_view v_cache, int64_t kv_len, const int32_t *kv_lens, void *out, float *lse, void *ws,
+           size_t ws_bytes, hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
+        return fail(LT_ERR_SHAPE, "bad decode sizes (B=%d Hq=%d Hkv=%d kv_len=%lld)", B, Hq, Hkv, (long long)kv_len);
+    if (dtype == LT_BF16 && Hq / Hkv > 16) return fail(LT_ERR_SHAPE, "bf16 decode supports Hq/Hkv <= 16");
+    if (kv_len > ((int64_t)1 << 40)) return fail(LT_ERR_SHAPE, "kv_len too large");
+    if (!(scale == scale) || isinf(scale)) return fail(LT_ERR_VALUE, "scale is not finite");
+    if (q == nullptr || out == nullptr) return fail(LT_ERR_NULL, "q/out is NULL");
+    if (!aligned16(q) || !aligned16(out)) return fail(LT_ERR_LAYOUT, "q/out not 16-byte aligned");
+    int e;
+    if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
+    const int n_parts = lt::decode_num_parts(B, Hkv, kv_len);
+    const size_t need = lt::decode_ws_bytes(B, Hq, D, n_parts);
+    if (ws == nullptr) return fail(LT_ERR_NULL, "workspace is NULL");
+    if (!aligned16(ws)) return fail(LT_ERR_LAYOUT, "workspace not 16-byte aligned");
+    if (ws_bytes < need) return fail(LT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    lt::DecodeArgs a{};
+    a.q = q; a.k = k_cache.data; a.v = v_cache.data;
+    a.k_sb = k_cache.sb; a.k_sh = k_cache.sh; a.k_sn = k_cache.sn;
+    a.v_sb = v_cache.sb; a.v_sh = v_cache.sh; a.v_sn = v_cache.sn;
+    a.o = out; a.lse = lse; a.ws = (float *)ws;
+    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
+    a.kv_len = kv_len; a.kv_lens = kv_lens; a.n_parts = n_parts;
+    a.part_keys = ((int64_t)B * kv_len + n_parts - 1) / n_parts;
+    a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
+    a.c = a.scale * 1.4426950408889634f;
+    return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
+}
+
+int compact(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, int B, int Hkv, int N, int D,
+            int dtype, int S, int R, const int32_t *lens, hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hkv < 1 || N < 1) return fail(LT_ERR_SHAPE, "B, Hkv, N must be >= 1");
+    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1");
+    int e;
+    if ((e = check_view(k_full, "k_full", dtype)) || (e = check_view(v_full, "v_full", dtype)) ||
+        (e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype)))
+        return e;
+    lt::CompactArgs a{};
+    a.kf = k_full.data; a.vf = v_full.data; a.ks = k_stream.data; a.vs = v_stream.data;
+    a.kf_sb = k_full.sb; a.kf_sh = k_full.sh; a.kf_sn = k_full.sn;
+    a.vf_sb = v_full.sb; a.vf_sh = v_full.sh; a.vf_sn = v_full.sn;
+    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
+    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
+    a.B = B; a.Hkv = Hkv; a.N = N; a.D = D; a.elem = elem_size(dtype); a.S = S; a.R = R;
+    a.rows_out = N <= S + R ? N : S + R;
+    a.seq_len = lens;
+    return hip_status(lt::launch_compact(a, stream), "compaction launch");
+}
+
+int append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new, int B, int Hkv, int D,
+           int dtype, int S, int R, int64_t pos, const int32_t *pos_dev, hipStream_t stream) {
+    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
+    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
+    if (B < 1 || Hkv < 1) return fail(LT_ERR_SHAPE, "B and Hkv must be >= 1");
+    if (S < 0 || R < 1 || pos < 0) return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, pos >= 0");
+    if (k_new == nullptr || v_new == nullptr) return fail(LT_ERR_NULL, "k_new/v_new is NULL");
+    if (!aligned16(k_new) || !aligned16(v_new)) return fail(LT_ERR_LAYOUT, "k_new/v_new not 16-byte aligned");
+    int e;
+    if ((e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype))) return e;
+    lt::AppendArgs a{};
+    a.kn = k_new; a.vn = v_new; a.ks = k_stream.data; a.vs = v_stream.data;
+    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
+    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
+    a.B = B; a.Hkv = Hkv; a.D = D; a.elem = elem_size(dtype);
+    a.slot = pos < S ? pos : S + (pos - S) % R;
+    a.S = S; a.R = R; a.pos = pos_dev;
+    return hip_status(lt::launch_append(a, stream), "append launch");
 }
 
 }  // namespace
@@ -101,41 +221,25 @@ const char *lt_last_error(void) { return g_err; }
 int lt_prefill_attn_lse_lazy(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
                              float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio,
                              hipStream_t stream) {
-    int e = check_shape(shape);
-    if (e) return e;
-    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
-        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
-        return e;
-    if (lse == nullptr) return fail(LT_ERR_NULL, "lse is NULL");
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
-    if (W < 0 || W > shape->N) return fail(LT_ERR_SHAPE, "W %d outside [0, N=%d]", W, shape->N);
-    if (W > 0 && (lazy_rows == nullptr || lazy_ratio == nullptr))
-        return fail(LT_ERR_NULL, "W > 0 needs lazy_rows and lazy_ratio");
-    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, W, lazy_rows);
-    const int mode = W > 0 ? lt::MODE_FULL_LAZY : lt::MODE_FULL;
-    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, mode, stream)
-                                            : lt::launch_attn_f32(a, shape->D, mode, stream);
-    if (he != hipSuccess) return hip_status(he, "prefill launch");
-    if (W > 0) {
-        he = lt::launch_lazy_reduce(lazy_rows, lazy_ratio, shape->B * shape->Hq, W, stream);
-        if (he != hipSuccess) return hip_status(he, "lazy reduce launch");
-    }
-    return ok();
+    return prefill(shape, nullptr, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream);
+}
+
+int lt_prefill_attn_lse_lazy_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
+                                    lt_view v, lt_view out, float *lse, int S, int R, int W,
+                                    float *lazy_rows, float *lazy_ratio, hipStream_t stream) {
+    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
+    return prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream);
 }
 
 int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
                       float *lse, int S, int R, hipStream_t stream) {
-    int e = check_shape(shape);
-    if (e) return e;
-    if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
-        (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
-        return e;
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
-    lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, 0, nullptr);
-    hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, lt::MODE_STREAM, stream)
-                                            : lt::launch_attn_f32(a, shape->D, lt::MODE_STREAM, stream);
-    if (he != hipSuccess) return hip_status(he, "streaming launch");
-    return ok();
+    return streaming(shape, nullptr, q, k, v, out, lse, S, R, stream);
+}
+
+int lt_streaming_attn_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k, lt_view v,
+                             lt_view out, float *lse, int S, int R, hipStream_t stream) {
+    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
+    return streaming(shape, seq_lens, q, k, v, out, lse, S, R, stream);
 }
 
 int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len, size_t *bytes) {
@@ -143,82 +247,48 @@ int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_l
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
         return fail(LT_ERR_SHAPE, "bad decode sizes");
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
-    *bytes = lt::decode_ws_bytes(B, Hq, D, lt::decode_num_splits(B, Hkv, kv_len));
+    *bytes = lt::decode_ws_bytes(B, Hq, D, lt::decode_num_parts(B, Hkv, kv_len));
     return ok();
 }
 
 int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
                           lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
                           void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
-    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
-    if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
-        return fail(LT_ERR_SHAPE, "bad decode sizes (B=%d Hq=%d Hkv=%d kv_len=%lld)", B, Hq, Hkv, (long long)kv_len);
-    if (dtype == LT_BF16 && Hq / Hkv > 16) return fail(LT_ERR_SHAPE, "bf16 decode supports Hq/Hkv <= 16");
-    if (kv_len > ((int64_t)1 << 40)) return fail(LT_ERR_SHAPE, "kv_len too large");
-    if (!(scale == scale) || isinf(scale)) return fail(LT_ERR_VALUE, "scale is not finite");
-    if (q == nullptr || out == nullptr) return fail(LT_ERR_NULL, "q/out is NULL");
-    if (!aligned16(q) || !aligned16(out)) return fail(LT_ERR_LAYOUT, "q/out not 16-byte aligned");
-    int e;
-    if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
-    const int n_splits = lt::decode_num_splits(B, Hkv, kv_len);
-    const size_t need = lt::decode_ws_bytes(B, Hq, D, n_splits);
-    if (ws == nullptr) return fail(LT_ERR_NULL, "workspace is NULL");
-    if (!aligned16(ws)) return fail(LT_ERR_LAYOUT, "workspace not 16-byte aligned");
-    if (ws_bytes < need) return fail(LT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-    lt::DecodeArgs a{};
-    a.q = q; a.k = k_cache.data; a.v = v_cache.data;
-    a.k_sb = k_cache.sb; a.k_sh = k_cache.sh; a.k_sn = k_cache.sn;
-    a.v_sb = v_cache.sb; a.v_sh = v_cache.sh; a.v_sn = v_cache.sn;
-    a.o = out; a.lse = lse; a.ws = (float *)ws;
-    a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
-    a.kv_len = kv_len; a.n_splits = n_splits;
-    a.keys_per_split = (kv_len + n_splits - 1) / n_splits;
-    a.keys_per_split = (a.keys_per_split + 63) / 64 * 64;
-    a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
-    a.c = a.scale * 1.4426950408889634f;
-    return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
+    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, ws, ws_bytes,
+                  stream);
+}
+
+int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
+                                 lt_view k_cache, lt_view v_cache, const int32_t *kv_lens, int64_t max_kv_len,
+                                 void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (kv_lens == nullptr) return fail(LT_ERR_NULL, "kv_lens is NULL");
+    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, max_kv_len, kv_lens, out, lse, ws,
+                  ws_bytes, stream);
 }
 
 int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, int B,
                             int Hkv, int N, int D, int dtype, int S, int R, hipStream_t stream) {
-    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
-    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
-    if (B < 1 || Hkv < 1 || N < 1) return fail(LT_ERR_SHAPE, "B, Hkv, N must be >= 1");
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1");
-    int e;
-    if ((e = check_view(k_full, "k_full", dtype)) || (e = check_view(v_full, "v_full", dtype)) ||
-        (e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype)))
-        return e;
-    lt::CompactArgs a{};
-    a.kf = k_full.data; a.vf = v_full.data; a.ks = k_stream.data; a.vs = v_stream.data;
-    a.kf_sb = k_full.sb; a.kf_sh = k_full.sh; a.kf_sn = k_full.sn;
-    a.vf_sb = v_full.sb; a.vf_sh = v_full.sh; a.vf_sn = v_full.sn;
-    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
-    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
-    a.B = B; a.Hkv = Hkv; a.N = N; a.D = D; a.elem = elem_size(dtype); a.S = S; a.R = R;
-    a.rows_out = N <= S + R ? N : S + R;
-    return hip_status(lt::launch_compact(a, stream), "compaction launch");
+    return compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R, nullptr, stream);
+}
+
+int lt_compact_kv_streaming_varlen(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream,
+                                   int B, int Hkv, int N, int D, int dtype, int S, int R,
+                                   const int32_t *seq_lens, hipStream_t stream) {
+    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
+    return compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R, seq_lens, stream);
 }
 
 int lt_stream_cache_append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
                            int B, int Hkv, int D, int dtype, int S, int R, int64_t pos,
                            hipStream_t stream) {
-    if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
-    if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
-    if (B < 1 || Hkv < 1) return fail(LT_ERR_SHAPE, "B and Hkv must be >= 1");
-    if (S < 0 || R < 1 || pos < 0) return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, pos >= 0");
-    if (k_new == nullptr || v_new == nullptr) return fail(LT_ERR_NULL, "k_new/v_new is NULL");
-    if (!aligned16(k_new) || !aligned16(v_new)) return fail(LT_ERR_LAYOUT, "k_new/v_new not 16-byte aligned");
-    int e;
-    if ((e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype))) return e;
-    lt::AppendArgs a{};
-    a.kn = k_new; a.vn = v_new; a.ks = k_stream.data; a.vs = v_stream.data;
-    a.ks_sb = k_stream.sb; a.ks_sh = k_stream.sh; a.ks_sn = k_stream.sn;
-    a.vs_sb = v_stream.sb; a.vs_sh = v_stream.sh; a.vs_sn = v_stream.sn;
-    a.B = B; a.Hkv = Hkv; a.D = D; a.elem = elem_size(dtype);
-    a.slot = pos < S ? pos : S + (pos - S) % R;
-    return hip_status(lt::launch_append(a, stream), "append launch");
+    return append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, pos, nullptr, stream);
+}
+
+int lt_stream_cache_append_varlen(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
+                                  int B, int Hkv, int D, int dtype, int S, int R, const int32_t *pos,
+                                  hipStream_t stream) {
+    if (pos == nullptr) return fail(LT_ERR_NULL, "pos is NULL");
+    return append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, 0, pos, stream);
 }
 
 int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64_t *full_bytes,

@@ -68,3 +68,42 @@ def stream_append(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new: torch.T
     api.lt_stream_cache_append(k_stream, v_stream, k_new.contiguous(), v_new.contiguous(), S, R, pos,
                                stream)
     return min(pos + 1, S + R)
+
+
+def _device_lens(lens, device) -> torch.Tensor:
+    if isinstance(lens, torch.Tensor):
+        return lens.to(device=device, dtype=torch.int32).contiguous()
+    return torch.tensor(list(lens), device=device, dtype=torch.int32)
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, seq_lens, S: int, R: int, W: int,
+                   scale: float = 0.0, stream=None):
+    """Padded variable-length batch; seq_lens: [B] lengths (list or tensor).
+    Returns (out, lse, lazy_rows, lazy_ratio); rows past a sequence's length
+    are left as torch.empty made them."""
+    B, Hq, N, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+    rows = ratio = None
+    if W > 0:
+        rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+        ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    api.lt_prefill_attn_lse_lazy_varlen(q, k, v, out, lse, _device_lens(seq_lens, q.device), S, R, W, rows,
+                                        ratio, scale, stream)
+    return out, lse, rows, ratio
+
+
+def decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, kv_lens,
+                  max_kv_len: Optional[int] = None, ws: Optional[torch.Tensor] = None, scale: float = 0.0,
+                  stream=None):
+    """Decode with per-sequence context lengths kv_lens [B] (<= max_kv_len,
+    by default the cache rows)."""
+    B, Hq, D = q.shape
+    L = k_cache.shape[2] if max_kv_len is None else max_kv_len
+    if ws is None:
+        ws = decode_workspace(B, Hq, k_cache.shape[1], D, L, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    api.lt_hybrid_decode_attn_varlen(q, k_cache, v_cache, _device_lens(kv_lens, q.device), L, out, lse, ws,
+                                     scale, stream)
+    return out, lse

@@ -21,6 +21,10 @@ contexts up to 100K tokens; real prompts and weights are not used):
             prompts (prompt 0 is driver64 itself); capacity 32
   decode100k bf16, B8, context 100000, 64 layers of Hq40 Hkv8 D128, seed 5;
             layers 0..31 full (100000 rows), 32..63 streaming (1024 rows)
+  qwen32k-varlen  four qwen32k prompts of 32768, 24576, 16384, 8192 tokens
+            padded to 32768, seed 6, sink keys x3
+  decode100k-varlen  the decode step with contexts 100000 * (8-b)/8 for
+            sequence b on the full layers
 """
 from __future__ import annotations
 
@@ -56,7 +60,15 @@ DRIVER64 = Workload("driver64", 1, 32768, 40, 8, 128, torch.bfloat16, 4000, 4, 1
 DECODE100K = Workload("decode100k", 8, 100000, 40, 8, 128, torch.bfloat16, 5, 4, 1020, 0,
                       extra={"layers": 64, "full_layers": 32})
 
-WORKLOADS = {w.name: w for w in (TINY, MISTRAL8K, QWEN32K, DRIVER64, DECODE100K)}
+# Variable-length batches (padded to the longest sequence): four qwen32k-shaped
+# prompts of 32K, 24K, 16K and 8K tokens; and the decode step with eight
+# contexts from 100000 down to 12500 tokens on the full layers.
+QWEN32K_VARLEN = Workload("qwen32k-varlen", 4, 32768, 40, 8, 128, torch.bfloat16, 6, 4, 1020, 128,
+                          sink_scale=3.0)
+QWEN32K_VARLEN_LENS = (32768, 24576, 16384, 8192)
+DECODE100K_VARLEN_LENS = tuple(100000 * (8 - b) // 8 for b in range(8))
+
+WORKLOADS = {w.name: w for w in (TINY, MISTRAL8K, QWEN32K, DRIVER64, DECODE100K, QWEN32K_VARLEN)}
 
 
 def _gen(seed: int, device) -> torch.Generator:

@@ -240,6 +240,39 @@ def test_select_offline_errors(L):
     assert L.lt_select_offline(ok.ctypes.data_as(fp), 2, 3, 4, 1, None, None) == _lib.LT_ERR_NULL
 
 
+def test_varlen_errors(L):
+    """The _varlen calls reject a NULL length array, then validate exactly as
+    the uniform calls do (nothing is launched: every case fails first)."""
+    shp = shape()
+    P = ctypes.byref
+    f = L.lt_prefill_attn_lse_lazy_varlen
+    assert f(P(shp), None, view(), view(), view(), view(), GOOD, 4, 8, 4, GOOD, GOOD, None) == _lib.LT_ERR_NULL
+    assert f(P(shape(D=96)), GOOD, view(), view(), view(), view(), GOOD, 4, 8, 4, GOOD, GOOD,
+             None) == _lib.LT_ERR_DTYPE
+    assert f(P(shp), GOOD, view(), view(), view(), view(), GOOD, 4, 8, 65, GOOD, GOOD, None) == _lib.LT_ERR_SHAPE
+    assert f(P(shp), GOOD, view(), view(), view(), view(), None, 4, 8, 4, GOOD, GOOD, None) == _lib.LT_ERR_NULL
+    assert f(P(shp), GOOD, view(sn=100), view(), view(), view(), GOOD, 4, 8, 4, GOOD, GOOD,
+             None) == _lib.LT_ERR_LAYOUT
+    g = L.lt_streaming_attn_varlen
+    assert g(P(shp), None, view(), view(), view(), view(), None, 4, 8, None) == _lib.LT_ERR_NULL
+    assert g(P(shp), GOOD, view(), view(), view(), view(), None, 4, 0, None) == _lib.LT_ERR_SHAPE
+    d = L.lt_hybrid_decode_attn_varlen
+    assert d(8, 40, 8, 128, _lib.LT_BF16, 0.0, GOOD, view(), view(), None, 1000, GOOD, None, GOOD, 1 << 30,
+             None) == _lib.LT_ERR_NULL
+    assert d(8, 40, 8, 128, _lib.LT_BF16, 0.0, GOOD, view(), view(), GOOD, 0, GOOD, None, GOOD, 1 << 30,
+             None) == _lib.LT_ERR_SHAPE
+    n = ctypes.c_size_t()
+    assert L.lt_hybrid_decode_workspace_bytes(8, 40, 8, 128, 1000, ctypes.byref(n)) == 0
+    assert d(8, 40, 8, 128, _lib.LT_BF16, 0.0, GOOD, view(), view(), GOOD, 1000, GOOD, None, GOOD,
+             n.value - 16, None) == _lib.LT_ERR_WORKSPACE
+    c = L.lt_compact_kv_streaming_varlen
+    assert c(view(), view(), view(), view(), 1, 8, 100, 128, _lib.LT_BF16, 4, 10, None, None) == _lib.LT_ERR_NULL
+    assert c(view(), view(), view(), view(), 1, 8, 100, 128, _lib.LT_BF16, 4, 0, GOOD, None) == _lib.LT_ERR_SHAPE
+    a = L.lt_stream_cache_append_varlen
+    assert a(view(), view(), GOOD, GOOD, 2, 2, 128, _lib.LT_BF16, 4, 60, None, None) == _lib.LT_ERR_NULL
+    assert a(view(), view(), GOOD + 8, GOOD, 2, 2, 128, _lib.LT_BF16, 4, 60, GOOD, None) == _lib.LT_ERR_LAYOUT
+
+
 def test_kv_bytes_matches_oracle(L):
     from kv_cache_compression_causal_amd import api
     for (B, Hkv, N, D, dt, S, R) in [(1, 8, 32768, 128, 1, 4, 1020), (8, 8, 100000, 128, 1, 4, 1020),

@@ -71,6 +71,47 @@ def test_decode100k_full_size(layer):
         assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
 
 
+def test_qwen32k_varlen_full_size():
+    """Prompts of 32K, 24K, 16K and 8K tokens padded to 32K, as the bench runs
+    them: sampled rows of every sequence (its own last W rows, first rows,
+    random rows) for a spread of heads, and each sampled head's lazy ratio."""
+    w, lens = synth.QWEN32K_VARLEN, synth.QWEN32K_VARLEN_LENS
+    print(f"workload {w.name}: lengths {lens}", flush=True)
+    q, k, v = synth.workload_qkv(w, device=DEV)
+    out, lse, rows, ratio = ops.prefill_varlen(q, k, v, lens, w.S, w.R, w.W)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    got_ratio = np64(ratio)
+    for b, n in enumerate(lens):
+        for h in (0, 13, 27, 39):
+            hk = h // G
+            pos = _sample_rows(n, w.W, 16, seed=5000 * b + h)
+            pt = torch.as_tensor(pos, device=DEV, dtype=torch.long)
+            r = oracle.rows(np64(k[b, hk, :n]), np64(v[b, hk, :n]), pos, np64(q[b, h][pt]), S=w.S, R=w.R)
+            assert_close(f"out b{b} h{h}", np64(out[b, h][pt]), r["out"], TOL_BF16_OUT)
+            assert_close(f"lse b{b} h{h}", np64(lse[b, h][pt]), r["lse"], TOL_BF16_LSE)
+            obs = pos >= n - w.W
+            assert_close(f"lazy rows b{b} h{h}", np64(rows[b, h])[pos[obs] - (n - w.W)], r["lazy"][obs],
+                         TOL_BF16_RATIO)
+            assert abs(got_ratio[b, h] - r["lazy"][obs].sum() / w.W) <= TOL_BF16_RATIO
+
+
+def test_decode100k_varlen_full_size():
+    """A full decode100k layer with the bench's eight contexts (100000 down to
+    12500 tokens): three (batch, KV head) groups against the oracle."""
+    w, lens = synth.DECODE100K, synth.DECODE100K_VARLEN_LENS
+    q, k, v = synth.decode_layer(0, w, device=DEV)
+    out, lse = ops.decode_varlen(q, k, v, lens)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hk in [(0, 0), (w.B - 1, w.Hkv - 1), (3, 5)]:
+        n = lens[b]
+        r = oracle.decode(np64(q[b:b + 1, hk * G:(hk + 1) * G]), np64(k[b:b + 1, hk:hk + 1, :n]),
+                          np64(v[b:b + 1, hk:hk + 1, :n]))
+        assert_close(f"decode out b{b} hk{hk}", np64(out[b:b + 1, hk * G:(hk + 1) * G]), r["out"], TOL_BF16_OUT)
+        assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
+
+
 @pytest.mark.parametrize("policy", ["after", "before"])
 def test_driver_small_stack(policy):
     """8 layers with the driver's sink/recency recipe at N=1024: per-layer ratios
