@@ -183,6 +183,23 @@ int lt_prefill_attn_lse_lazy_varlen(const lt_shape *shape, const int32_t *seq_le
                                     lt_view k, lt_view v, lt_view out, float *lse, int S, int R,
                                     int W, float *lazy_rows, float *lazy_ratio, hipStream_t stream);
 
+/*
+ * Prefill that also writes the layer's streaming slice ([P1] solution 2,
+ * [P4] Figure 2: the KV of a layer that turns out lazy is cut to its sink +
+ * recent rows; producing that slice in the prefill itself makes the later
+ * switch a release of the full buffers, with no copy kernel).  Everything
+ * lt_prefill_attn_lse_lazy (or, with seq_lens, its _varlen form) computes,
+ * plus: k_stream / v_stream [B,Hkv,>=min(len,S+R),D] receive the K/V rows of
+ * positions [0,S) and [len-R,len) of every (b, kv head) in the slot order of
+ * lt_compact_kv_streaming, i.e. exactly what that call would write.
+ * seq_lens: device int32 [B] or NULL (every sequence has N rows).  The two
+ * views are checked like the others (LT_ERR_NULL, LT_ERR_LAYOUT).
+ */
+int lt_prefill_attn_lse_lazy_emit(const lt_shape *shape, const int32_t *seq_lens, lt_view q,
+                                  lt_view k, lt_view v, lt_view out, float *lse, int S, int R,
+                                  int W, float *lazy_rows, float *lazy_ratio, lt_view k_stream,
+                                  lt_view v_stream, hipStream_t stream);
+
 /* Streaming attention over a padded variable-length batch (seq_lens [B]). */
 int lt_streaming_attn_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
                              lt_view v, lt_view out, float *lse, int S, int R, hipStream_t stream);

@@ -23,7 +23,7 @@ EXPORTS = (
     "lt_last_error", "lt_probe_mfma_bf16", "lt_probe_read", "lt_lazy_queue_create_policy",
     "lt_select_lazy_layers_policy", "lt_stream_cache_append", "lt_select_offline",
     "lt_prefill_attn_lse_lazy_varlen", "lt_streaming_attn_varlen", "lt_hybrid_decode_attn_varlen",
-    "lt_compact_kv_streaming_varlen", "lt_stream_cache_append_varlen",
+    "lt_compact_kv_streaming_varlen", "lt_stream_cache_append_varlen", "lt_prefill_attn_lse_lazy_emit",
 )
 
 
@@ -108,6 +108,10 @@ def lib() -> ctypes.CDLL:
     L.lt_streaming_attn_varlen.argtypes = [ctypes.POINTER(LtShape), c_void_p, LtView, LtView, LtView, LtView,
                                            c_void_p, c_int, c_int, c_void_p]
     L.lt_streaming_attn_varlen.restype = c_int
+    L.lt_prefill_attn_lse_lazy_emit.argtypes = [ctypes.POINTER(LtShape), c_void_p, LtView, LtView, LtView,
+                                                LtView, c_void_p, c_int, c_int, c_int, c_void_p, c_void_p,
+                                                LtView, LtView, c_void_p]
+    L.lt_prefill_attn_lse_lazy_emit.restype = c_int
     L.lt_hybrid_decode_attn_varlen.argtypes = [c_int, c_int, c_int, c_int, c_int, ctypes.c_float, c_void_p,
                                                LtView, LtView, c_void_p, c_int64, c_void_p, c_void_p,
                                                c_void_p, c_size_t, c_void_p]

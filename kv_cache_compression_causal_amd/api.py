@@ -171,6 +171,31 @@ def lt_prefill_attn_lse_lazy_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.T
                                                 W, _ptr(lazy_rows), _ptr(lazy_ratio), _stream(stream)))
 
 
+def lt_prefill_attn_lse_lazy_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                  lse: torch.Tensor, S: int, R: int, W: int, lazy_rows: Optional[torch.Tensor],
+                                  lazy_ratio: Optional[torch.Tensor], k_stream: torch.Tensor,
+                                  v_stream: torch.Tensor, seq_lens: Optional[torch.Tensor] = None,
+                                  scale: float = 0.0, stream=None) -> None:
+    """Prefill + LSE + lazy ratio that also writes the layer's streaming
+    slice into k_stream / v_stream [B, Hkv, >= min(N, S+R), D] (seq_lens:
+    optional int32 [B] device lengths of a padded batch)."""
+    _same_dtype(q, k, v, out, k_stream, v_stream)
+    B, Hq, N, D = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != N or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v, out")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (B, Hq, N):
+        raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
+    for t in (k_stream, v_stream):
+        if t.dim() != 4 or t.shape[0] != B or t.shape[1] != k.shape[1] or t.shape[2] < min(N, S + R) \
+                or t.shape[3] != D:
+            raise ValueError("streaming cache must be [B, Hkv, >= min(N, S+R), D]")
+    lens = 0 if seq_lens is None else _lens(seq_lens, B, "seq_lens")
+    shp = _shape(q, k, scale)
+    check(lib().lt_prefill_attn_lse_lazy_emit(ctypes.byref(shp), lens or None, _view(q), _view(k), _view(v),
+                                              _view(out), _ptr(lse), S, R, W, _ptr(lazy_rows), _ptr(lazy_ratio),
+                                              _view(k_stream), _view(v_stream), _stream(stream)))
+
+
 def lt_streaming_attn_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                              lse: Optional[torch.Tensor], seq_lens: torch.Tensor, S: int, R: int,
                              scale: float = 0.0, stream=None) -> None:

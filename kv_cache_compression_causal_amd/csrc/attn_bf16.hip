@@ -523,6 +523,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 a.lazy_rows[((int64_t)b * a.Hq + head[rb]) * a.W + (pos[rb] - (N - a.W))] = zt * inv;
         }
     }
+
+    // Streaming slice of this layer's KV (full attention, when asked for):
+    // the workgroup holding flattened row p*G copies position p, so every
+    // position has exactly one writer.  The workgroups of the last positions
+    // run first (longest-first order), so this stays off the kernel's tail.
+    if (MODE != MODE_STREAM) {
+        const StreamOut so = stream_out_late();
+        if (so.k != nullptr) {
+            const int p_lo = (r0 + G - 1) / G;
+            const int p_end = (r0 + BROWS + G - 1) / G;
+            emit_stream_rows<64 * NW>((const char *)kbase, (const char *)vbase, a.k_sn, a.v_sn, so, b, hk, N, a.S,
+                                      a.R, p_lo, p_end < N ? p_end : N, 2, D * 2, tid);
+        }
+    }
 }
 
 // Per-head lazy ratio: mean of the observed rows, summed in row order.  A

@@ -157,6 +157,15 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgs a) {
         }
         if (obs && half == 0) a.lazy_rows[((int64_t)b * a.Hq + h) * a.W + (i - (N - a.W))] = acc;
     }
+
+    // Streaming slice (full attention, when asked for): the blocks of the
+    // group's first query head copy their positions' K/V rows.
+    if (MODE != MODE_STREAM && h % a.G == 0) {
+        const StreamOut so = stream_out_late();
+        if (so.k != nullptr)
+            emit_stream_rows<64>((const char *)kbase, (const char *)vbase, a.k_sn, a.v_sn, so, b, hk, N, a.S, a.R, q0,
+                                 q0 + ROWS < N ? q0 + ROWS : N, 4, D * 4, lane);
+    }
 }
 
 template <int D>

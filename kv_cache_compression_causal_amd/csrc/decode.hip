@@ -90,13 +90,12 @@ __device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Total keys T of one head over the batch and the part size Q = ceil(T/P)
-// (given by the host when every context has the same length).
+// Per-sequence contexts (kv_lens): total keys T of one head over the batch
+// and the part size Q = ceil(T/P).
 struct Partition {
     int64_t T, Q;
 };
 __device__ __forceinline__ Partition partition(const DecodeArgs &a) {
-    if (a.kv_lens == nullptr) return Partition{(int64_t)a.B * a.kv_len, a.part_keys};
     int64_t T = 0;
     for (int b = 0; b < a.B; ++b) T += ctx_len(a, b);
     return Partition{T, T > 0 ? div_nonneg(T + a.n_parts - 1, a.n_parts) : 0};
@@ -104,7 +103,6 @@ __device__ __forceinline__ Partition partition(const DecodeArgs &a) {
 
 // First key of sequence b in the end-to-end order.
 __device__ __forceinline__ int64_t ctx_start(const DecodeArgs &a, int b) {
-    if (a.kv_lens == nullptr) return (int64_t)b * a.kv_len;
     int64_t S = 0;
     for (int i = 0; i < b; ++i) S += ctx_len(a, i);
     return S;
@@ -126,20 +124,11 @@ __device__ __forceinline__ void for_each_segment(const DecodeArgs &a, int part, 
     if (g0 >= pt.T) return;
     const int64_t g1 = g0 + pt.Q < pt.T ? g0 + pt.Q : pt.T;
     // The sequence holding key g0.
-    int b;
-    int64_t S, n;
-    if (a.kv_lens == nullptr) {
-        b = (int)div_nonneg(g0, a.kv_len);
-        S = (int64_t)b * a.kv_len;
-        n = a.kv_len;
-    } else {
-        b = 0;
-        S = 0;
-        n = ctx_len(a, 0);
-        while (b + 1 < a.B && S + n <= g0) {
-            S += n;
-            n = ctx_len(a, ++b);
-        }
+    int b = 0;
+    int64_t S = 0, n = ctx_len(a, 0);
+    while (b + 1 < a.B && S + n <= g0) {
+        S += n;
+        n = ctx_len(a, ++b);
     }
     f(b, g0 - S, (g1 < S + n ? g1 : S + n) - S, part + b);
     // Sequences after it that the part still reaches.
@@ -163,7 +152,11 @@ __device__ __forceinline__ void for_each_segment(const DecodeArgs &a, int part, 
 // load-counter waits stay exact (mixing in direct global->LDS loads made it
 // wait for every outstanding load).  No workgroup barrier until the four
 // waves merge their states at the end of the segment.
-template <int D>
+// UNIFORM (every context kv_len long): workgroup (split, b*Hkv + kv head)
+// streams keys [split*kps, (split+1)*kps) of sequence b, kps = part_keys, and
+// writes slot b*splits + split + b.  Otherwise (kv_lens): workgroup (part,
+// kv head) streams its part of the end-to-end keys (for_each_segment).
+template <int D, bool UNIFORM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;       // 32-dim steps (Q.K)
     constexpr int DB = D / 16;       // 16-dim blocks (O)
@@ -184,13 +177,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     // scalar branches and the load counters are tracked exactly across them.
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
-    const int hk = blockIdx.x;    // KV heads fastest: with 8 of them each XCD streams one
-    const int part = blockIdx.y;
+    const int hk = UNIFORM ? (int)(blockIdx.y % a.Hkv) : (int)blockIdx.y;
     read_now(a.q), read_now(a.k), read_now(a.v), read_now(a.ws);
     read_now(a.k_sb), read_now(a.k_sh), read_now(a.k_sn);
     read_now(a.v_sb), read_now(a.v_sh), read_now(a.v_sn);
     read_now(a.B), read_now(a.Hq), read_now(a.G), read_now(a.c);
-    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts);
+    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts), read_now(a.splits);
     const int G = a.G;
     const float c = a.c;
     bf16 *const slot = (bf16 *)smem + wave * VTILE;
@@ -365,18 +357,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     }
     __syncthreads();  // the merge buffers share LDS with the next segment's V slots
     };
-    for_each_segment(a, part, segment);
+    if constexpr (UNIFORM) {
+        const int split = blockIdx.x, b = (int)(blockIdx.y / a.Hkv);
+        const int64_t kbeg = (int64_t)split * a.part_keys;
+        const int64_t kend = kbeg + a.part_keys < a.kv_len ? kbeg + a.part_keys : a.kv_len;
+        if (kbeg < kend) segment(b, kbeg, kend, b * a.splits + split + b);
+    } else {
+        for_each_segment(a, (int)blockIdx.x, segment);
+    }
 }
 
 // fp32: block of 64 lanes per (query head, part), looping over the part's
 // segments; lane owns dims lane, lane+64.
-template <int D>
+template <int D, bool UNIFORM>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
-    const int h = blockIdx.x, hk = h / a.G;
-    const int part = blockIdx.y;
-    for_each_segment(a, part, [&](int b, int64_t kbeg, int64_t kend, int ws_slot) {
+    const int h = UNIFORM ? (int)(blockIdx.y % a.Hq) : (int)blockIdx.y, hk = h / a.G;
+    auto segment = [&](int b, int64_t kbeg, int64_t kend, int ws_slot) {
         const float *kbase = (const float *)a.k + b * a.k_sb + (int64_t)hk * a.k_sh;
         const float *vbase = (const float *)a.v + b * a.v_sb + (int64_t)hk * a.v_sh;
         float q[PER], o[PER];
@@ -408,7 +406,15 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             dst[D] = m;
             dst[D + 1] = l;
         }
-    });
+    };
+    if constexpr (UNIFORM) {
+        const int split = blockIdx.x, b = (int)(blockIdx.y / a.Hq);
+        const int64_t kbeg = (int64_t)split * a.part_keys;
+        const int64_t kend = kbeg + a.part_keys < a.kv_len ? kbeg + a.part_keys : a.kv_len;
+        if (kbeg < kend) segment(b, kbeg, kend, b * a.splits + split + b);
+    } else {
+        for_each_segment(a, (int)blockIdx.x, segment);
+    }
 }
 
 // Merge split partials: out = sum_s w_s o_s / sum_s w_s, w_s = l_s 2^(m_s - M);
@@ -421,16 +427,21 @@ template <int D, typename T>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     constexpr int CH = 16;
     read_now(a.ws), read_now(a.o), read_now(a.lse), read_now(a.B), read_now(a.Hq);
-    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts);
+    read_now(a.kv_len), read_now(a.kv_lens), read_now(a.part_keys), read_now(a.n_parts), read_now(a.splits);
     const int bh = blockIdx.x;
     const int b = bh / a.Hq, h = bh % a.Hq;
     const int d = threadIdx.x;
-    // Sequence b's partial states: the parts p0..p1 its context overlaps, in
-    // slots p0 + b .. p1 + b (none for an empty context).
-    const Partition pt = partition(a);
-    const int64_t S = ctx_start(a, b), len = ctx_len(a, b);
-    const int64_t p0 = len > 0 ? div_nonneg(S, pt.Q) : 0;
-    const int n = len > 0 ? (int)(div_nonneg(S + len - 1, pt.Q) - p0) + 1 : 0;
+    // Sequence b's partial states in consecutive slots: its `splits` splits
+    // from slot b*splits + b (uniform contexts), or the parts p0..p1 its
+    // context overlaps, in slots p0 + b .. p1 + b (none for an empty one).
+    int64_t p0 = (int64_t)b * a.splits;
+    int n = a.splits;
+    if (a.kv_lens != nullptr) {
+        const Partition pt = partition(a);
+        const int64_t S = ctx_start(a, b), len = ctx_len(a, b);
+        p0 = len > 0 ? div_nonneg(S, pt.Q) : 0;
+        n = len > 0 ? (int)(div_nonneg(S + len - 1, pt.Q) - p0) + 1 : 0;
+    }
     const int64_t stride = (int64_t)a.Hq * (D + 2);
     const float *src = a.ws + (p0 + b) * stride + (int64_t)h * (D + 2);
     float M = kNegInf, L = 0.f, O = 0.f;
@@ -468,6 +479,23 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 
 }  // namespace
 
+int64_t decode_split_keys(int64_t kv_len, int splits) {
+    const int64_t kps = (kv_len + splits - 1) / splits;
+    return (kps + kTile - 1) / kTile * kTile;
+}
+
+int decode_num_splits(int B, int Hkv, int64_t kv_len) {
+    // Every context kv_len long: about 512 workgroups (two per CU) over the
+    // B*Hkv (sequence, KV head) pairs, splits of a multiple of kTile keys.
+    const int64_t units = (int64_t)B * Hkv;
+    int64_t want = (512 + units - 1) / units;
+    const int64_t max_splits = (kv_len + kTile - 1) / kTile;
+    if (want > max_splits) want = max_splits;
+    if (want < 1) want = 1;
+    const int64_t kps = decode_split_keys(kv_len, (int)want);
+    return (int)((kv_len + kps - 1) / kps);
+}
+
 int decode_num_parts(int B, int Hkv, int64_t kv_len) {
     // Aim for about 512 workgroups (two per CU, eight waves streaming their
     // own steps) so enough loads are in flight to cover HBM latency; parts
@@ -483,26 +511,35 @@ size_t decode_ws_bytes(int B, int Hq, int D, int n_parts) {
     return (size_t)(n_parts + B - 1) * Hq * (D + 2) * sizeof(float);
 }
 
-hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
+namespace {
+template <int D>
+void launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
+    const bool uni = a.kv_lens == nullptr;
     if (dtype == LT_BF16) {
-        dim3 grid((unsigned)a.Hkv, (unsigned)a.n_parts);
-        if (a.D == 64) {
-            hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, dim3(256), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<64, bf16>), dim3(a.B * a.Hq), dim3(64), 0, st, a);
-        } else {
-            hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, dim3(256), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<128, bf16>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
-        }
+        const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv))
+                              : dim3((unsigned)a.n_parts, (unsigned)a.Hkv);
+        if (uni)
+            hipLaunchKernelGGL((decode_bf16_kernel<D, true>), grid, dim3(256), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_bf16_kernel<D, false>), grid, dim3(256), 0, st, a);
+        hipLaunchKernelGGL((decode_combine_kernel<D, bf16>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     } else {
-        dim3 grid((unsigned)a.Hq, (unsigned)a.n_parts);
-        if (a.D == 64) {
-            hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(64), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<64, float>), dim3(a.B * a.Hq), dim3(64), 0, st, a);
-        } else {
-            hipLaunchKernelGGL(decode_f32_kernel<128>, grid, dim3(64), 0, st, a);
-            hipLaunchKernelGGL((decode_combine_kernel<128, float>), dim3(a.B * a.Hq), dim3(128), 0, st, a);
-        }
+        const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hq))
+                              : dim3((unsigned)a.n_parts, (unsigned)a.Hq);
+        if (uni)
+            hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     }
+}
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
+    if (a.D == 64)
+        launch_decode_d<64>(a, dtype, st);
+    else
+        launch_decode_d<128>(a, dtype, st);
     return hipGetLastError();
 }
 

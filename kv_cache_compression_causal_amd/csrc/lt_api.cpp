@@ -72,6 +72,7 @@ lt::AttnArgs make_args(const lt_shape *s, const lt_view &q, const lt_view &k, co
     a.c = a.scale * 1.4426950408889634f;
     a.S = S; a.R = R; a.W = W;
     a.seq_len = nullptr;
+    a.st = lt::StreamOut{};
     return a;
 }
 
@@ -79,7 +80,8 @@ lt::AttnArgs make_args(const lt_shape *s, const lt_view &q, const lt_view &k, co
 // `lens` is a device array of B lengths or nullptr.
 
 int prefill(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt_view v, lt_view out,
-            float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio, hipStream_t stream) {
+            float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio, hipStream_t stream,
+            const lt_view *k_st = nullptr, const lt_view *v_st = nullptr) {
     int e = check_shape(shape);
     if (e) return e;
     if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
@@ -90,8 +92,13 @@ int prefill(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt
     if (W < 0 || W > shape->N) return fail(LT_ERR_SHAPE, "W %d outside [0, N=%d]", W, shape->N);
     if (W > 0 && (lazy_rows == nullptr || lazy_ratio == nullptr))
         return fail(LT_ERR_NULL, "W > 0 needs lazy_rows and lazy_ratio");
+    if (k_st != nullptr && ((e = check_view(*k_st, "k_stream", shape->dtype)) ||
+                            (e = check_view(*v_st, "v_stream", shape->dtype))))
+        return e;
     lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, W, lazy_rows);
     a.seq_len = lens;
+    if (k_st != nullptr)
+        a.st = lt::StreamOut{k_st->data, v_st->data, k_st->sb, k_st->sh, k_st->sn, v_st->sb, v_st->sh, v_st->sn};
     const int mode = W > 0 ? lt::MODE_FULL_LAZY : lt::MODE_FULL;
     hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, mode, stream)
                                             : lt::launch_attn_f32(a, shape->D, mode, stream);
@@ -120,6 +127,15 @@ int streaming(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, 
     return ok();
 }
 
+// Workspace of a decode call at these sizes: enough for either layout (per-
+// sequence splits for uniform contexts, equal parts for per-sequence ones),
+// so one workspace serves both calls.
+size_t decode_ws_need(int B, int Hq, int Hkv, int D, int64_t kv_len) {
+    const size_t uni = lt::decode_ws_bytes(B, Hq, D, B * lt::decode_num_splits(B, Hkv, kv_len));
+    const size_t var = lt::decode_ws_bytes(B, Hq, D, lt::decode_num_parts(B, Hkv, kv_len));
+    return uni > var ? uni : var;
+}
+
 int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q, lt_view k_cache,
            lt_view v_cache, int64_t kv_len, const int32_t *kv_lens, void *out, float *lse, void *ws,
            size_t ws_bytes, hipStream_t stream) {
@@ -134,8 +150,7 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     if (!aligned16(q) || !aligned16(out)) return fail(LT_ERR_LAYOUT, "q/out not 16-byte aligned");
     int e;
     if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
-    const int n_parts = lt::decode_num_parts(B, Hkv, kv_len);
-    const size_t need = lt::decode_ws_bytes(B, Hq, D, n_parts);
+    const size_t need = decode_ws_need(B, Hq, Hkv, D, kv_len);
     if (ws == nullptr) return fail(LT_ERR_NULL, "workspace is NULL");
     if (!aligned16(ws)) return fail(LT_ERR_LAYOUT, "workspace not 16-byte aligned");
     if (ws_bytes < need) return fail(LT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -145,8 +160,16 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     a.v_sb = v_cache.sb; a.v_sh = v_cache.sh; a.v_sn = v_cache.sn;
     a.o = out; a.lse = lse; a.ws = (float *)ws;
     a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D;
-    a.kv_len = kv_len; a.kv_lens = kv_lens; a.n_parts = n_parts;
-    a.part_keys = ((int64_t)B * kv_len + n_parts - 1) / n_parts;
+    a.kv_len = kv_len; a.kv_lens = kv_lens;
+    if (kv_lens == nullptr) {  // every context kv_len long: per-sequence splits
+        a.splits = lt::decode_num_splits(B, Hkv, kv_len);
+        a.part_keys = lt::decode_split_keys(kv_len, a.splits);
+        a.n_parts = B * a.splits;
+    } else {                   // per-sequence contexts: equal parts of the batch
+        a.splits = 0;
+        a.part_keys = 0;
+        a.n_parts = lt::decode_num_parts(B, Hkv, kv_len);
+    }
     a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
     a.c = a.scale * 1.4426950408889634f;
     return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
@@ -231,6 +254,13 @@ int lt_prefill_attn_lse_lazy_varlen(const lt_shape *shape, const int32_t *seq_le
     return prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream);
 }
 
+int lt_prefill_attn_lse_lazy_emit(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
+                                  lt_view v, lt_view out, float *lse, int S, int R, int W, float *lazy_rows,
+                                  float *lazy_ratio, lt_view k_stream, lt_view v_stream, hipStream_t stream) {
+    return prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream, &k_stream,
+                   &v_stream);
+}
+
 int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
                       float *lse, int S, int R, hipStream_t stream) {
     return streaming(shape, nullptr, q, k, v, out, lse, S, R, stream);
@@ -247,7 +277,7 @@ int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_l
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
         return fail(LT_ERR_SHAPE, "bad decode sizes");
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
-    *bytes = lt::decode_ws_bytes(B, Hq, D, lt::decode_num_parts(B, Hkv, kv_len));
+    *bytes = decode_ws_need(B, Hq, Hkv, D, kv_len);
     return ok();
 }
 

@@ -45,19 +45,24 @@ class DriverResult:
     stream_bytes: int
     prefill_ms: List[float] = field(default_factory=list)
     wall_s: float = 0.0
+    streaming_kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = field(default_factory=dict)  # layer -> (k, v)
 
 
 def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Tensor]], layers: int,
         capacity: int, S: int, R: int, W: int, timing: bool = False,
-        policy: int = LT_EVICT_AFTER_PUSH) -> DriverResult:
+        policy: int = LT_EVICT_AFTER_PUSH, emit: bool = False) -> DriverResult:
     """Run the layer stack.  ``layer_inputs(l)`` returns (q, k, v) for layer l
     on the device; the layer's k, v are its KV cache.  policy: the queue's
     eviction timing (LT_EVICT_AFTER_PUSH or LT_EVICT_BEFORE_PUSH).  With
     eviction before the push the victim does not depend on the current layer,
-    so its KV counts as freed before the current layer's KV is stored."""
+    so its KV counts as freed before the current layer's KV is stored.
+    emit: every layer's prefill also writes its streaming slice
+    (lt_prefill_attn_lse_lazy_emit); switching a layer then only releases its
+    full KV (no compaction), and a layer at full size holds its slice too."""
     queue = api.LazyQueue(layers, capacity, policy)
     kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
     streaming_kv: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}
+    slices: Dict[int, Tuple[torch.Tensor, torch.Tensor]] = {}   # emitted, for layers still at full size
     head_ratio, scores, evicted, retained, transient, times = [], [], [], [], [], []
     is_stream = [0] * layers
     full_b = stream_b = 0
@@ -78,7 +83,14 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-        api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
+        if emit:
+            n_slots = min(N, S + R)
+            ks = torch.empty(B, Hkv, n_slots, D, device=q.device, dtype=q.dtype)
+            vs = torch.empty_like(ks)
+            api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, ks, vs)
+            slices[l] = (ks, vs)
+        else:
+            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
         if timing:
             e1.record()
         r = ratio.reshape(-1).cpu().numpy()   # the per-layer device -> host sync
@@ -88,22 +100,27 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
         del q
         ev, score = queue.push_ratios(l, r)
         freed_first = policy == LT_EVICT_BEFORE_PUSH and 0 <= ev < l
-        held = sum(stream_b if (is_stream[x] or (freed_first and x == ev)) else full_b
-                   for x in range(l)) + full_b
+        at_full = full_b + stream_b if emit else full_b
+        held = sum(stream_b if (is_stream[x] or (freed_first and x == ev)) else at_full
+                   for x in range(l)) + at_full
         transient.append(held)
         if ev >= 0:
             kf, vf = kv.pop(ev)
-            streaming_kv[ev] = ops.compact(kf, vf, S, R)
+            if emit:
+                streaming_kv[ev] = slices.pop(ev)   # written by its prefill: nothing to copy
+            else:
+                streaming_kv[ev] = ops.compact(kf, vf, S, R)
             del kf, vf   # the full KV of the evicted layer is released
             is_stream[ev] = 1
         head_ratio.append([float(x) for x in r])
         scores.append(score)
         evicted.append(ev)
-        retained.append(sum(stream_b if is_stream[x] else full_b for x in range(l + 1)))
+        retained.append(sum(stream_b if is_stream[x] else (full_b + stream_b if emit else full_b)
+                            for x in range(l + 1)))
     torch.cuda.synchronize()
     queue.close()
     return DriverResult(layers, capacity, head_ratio, scores, evicted, is_stream, retained, transient,
-                        full_b, stream_b, times, time.perf_counter() - t_start)
+                        full_b, stream_b, times, time.perf_counter() - t_start, streaming_kv)
 
 
 @dataclass

@@ -107,3 +107,24 @@ def decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     api.lt_hybrid_decode_attn_varlen(q, k_cache, v_cache, _device_lens(kv_lens, q.device), L, out, lse, ws,
                                      scale, stream)
     return out, lse
+
+
+def prefill_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int, R: int, W: int, seq_lens=None,
+                 slots: Optional[int] = None, scale: float = 0.0, stream=None):
+    """Prefill + LSE + lazy ratio that also writes the streaming slice.
+    Returns (out, lse, lazy_rows, lazy_ratio, k_stream, v_stream); the
+    streaming cache has min(N, S+R) rows, or `slots` (>= that) for a cache
+    that decode will keep appending to."""
+    B, Hq, N, D = q.shape
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+    rows = ratio = None
+    if W > 0:
+        rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+        ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    n_slots = min(N, S + R) if slots is None else max(slots, min(N, S + R))
+    ks = torch.empty(B, k.shape[1], n_slots, D, device=q.device, dtype=q.dtype)
+    vs = torch.empty_like(ks)
+    lens = None if seq_lens is None else _device_lens(seq_lens, q.device)
+    api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, ks, vs, lens, scale, stream)
+    return out, lse, rows, ratio, ks, vs

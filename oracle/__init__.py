@@ -377,13 +377,15 @@ def kv_bytes(B: int, Hkv: int, N: int, D: int, elem: int, S: int, R: int) -> Tup
 
 
 def kv_accounting(evicted_at_step: Sequence[int], full: int, stream: int,
-                  policy: str = "after") -> Dict[str, List[int]]:
+                  policy: str = "after", emit: bool = False) -> Dict[str, List[int]]:
     """Per-step KV bytes while prefill walks the layers.
 
     transient[l]: every layer so far at its current size plus layer l at full
     size, before the queue's pop -- except that with eviction before the push
     a victim from an earlier layer is already streaming (its memory is freed
-    for layer l).  retained[l]: the same after the pop."""
+    for layer l).  retained[l]: the same after the pop.  With ``emit`` every
+    layer's prefill also produced its streaming slice, so a layer still at
+    full size holds full + stream bytes (and switching it keeps the slice)."""
     L = len(evicted_at_step)
     is_stream = [False] * L
     retained, transient = [], []
@@ -391,10 +393,11 @@ def kv_accounting(evicted_at_step: Sequence[int], full: int, stream: int,
         ev = evicted_at_step[l]
         if policy == "before" and 0 <= ev < l:
             is_stream[ev] = True
-        before = sum(stream if is_stream[x] else full for x in range(l)) + full
+        at_full = full + stream if emit else full
+        before = sum(stream if is_stream[x] else at_full for x in range(l)) + at_full
         if ev >= 0:
             is_stream[ev] = True
-        after = sum(stream if is_stream[x] else full for x in range(l + 1))
+        after = sum(stream if is_stream[x] else at_full for x in range(l + 1))
         transient.append(before)
         retained.append(after)
     return {"transient": transient, "retained": retained}

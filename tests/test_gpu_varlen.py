@@ -125,7 +125,10 @@ def test_decode_varlen(Hq, Hkv, D, L, dtype, lens, seed):
         assert_close(f"decode lse b{b}", np64(lse[b]), ref["lse"][b], tl)
 
 
-def test_decode_varlen_full_lengths_equal_uniform_call():
+def test_decode_varlen_full_lengths_agree_with_uniform_call():
+    """All contexts at full length: the varlen call (equal parts of the
+    batch) and the uniform call (per-sequence splits) sum in different
+    pieces, so they agree to rounding, not bit for bit."""
     g = torch.Generator().manual_seed(46)
     q = torch.randn(3, 10, 128, generator=g).to(torch.bfloat16).to(DEV)
     k = torch.randn(3, 2, 3000, 128, generator=g).to(torch.bfloat16).to(DEV)
@@ -133,7 +136,8 @@ def test_decode_varlen_full_lengths_equal_uniform_call():
     a = ops.decode(q, k, v)
     b = ops.decode_varlen(q, k, v, [3000] * 3)
     torch.cuda.synchronize()
-    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert_close("out", np64(b[0]), np64(a[0]), TOL_BF16_OUT)
+    assert_close("lse", np64(b[1]), np64(a[1]), 1e-4)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])

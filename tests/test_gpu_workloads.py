@@ -153,6 +153,29 @@ def test_driver_small_stack(policy):
     assert (res.full_bytes, res.stream_bytes) == (full, stream)
 
 
+def test_driver_emitted_slices_match_compaction():
+    """The driver with slices written by each layer's prefill: the same
+    ratios and decisions as with compaction, every converted layer's cache
+    bit-identical to the compacted one, and the KV accounting of the oracle
+    with emitted slices."""
+    print("driver small stack, emitted slices", flush=True)
+    w = synth.Workload("driver-small", 1, 1024, 10, 2, 128, torch.bfloat16, 4000, 4, 100, 32,
+                       extra={"layers": 8, "capacity": 4})
+
+    def inputs(l):
+        q, k, v, _, _ = synth.driver_layer(l, w, device=DEV, recent=w.R)
+        return q, k, v
+
+    base = driver.run(inputs, 8, 4, w.S, w.R, w.W)
+    emit = driver.run(inputs, 8, 4, w.S, w.R, w.W, emit=True)
+    assert emit.head_ratio == base.head_ratio and emit.evicted_at_step == base.evicted_at_step
+    assert sorted(emit.streaming_kv) == sorted(base.streaming_kv) and len(emit.streaming_kv) == 4
+    for l, (ks, vs) in base.streaming_kv.items():
+        assert torch.equal(emit.streaming_kv[l][0], ks) and torch.equal(emit.streaming_kv[l][1], vs)
+    acc = oracle.kv_accounting(emit.evicted_at_step, emit.full_bytes, emit.stream_bytes, emit=True)
+    assert acc["retained"] == emit.retained_bytes and acc["transient"] == emit.transient_bytes
+
+
 @pytest.mark.gpu
 def test_offline_selection_small_stack():
     """Offline selection over 3 prompts of an 8-layer stack at N=1024: every

@@ -195,3 +195,22 @@ def test_kv_accounting_before_push():
     ev0, _ = oracle.select_lazy_layers(scores, 0, policy="before")
     acc0 = oracle.kv_accounting(ev0, full, stream, policy="before")
     assert all(t == full + l * stream for l, t in enumerate(acc0["transient"]))
+
+
+def test_kv_accounting_with_emitted_slices():
+    """With the streaming slice written by every layer's prefill, a layer at
+    full size also holds its 4 MiB slice: final 32 x 132 + 32 x 4 = 4352 MiB,
+    peak 33 x 132 + 31 x 4 = 4480 MiB (after push), 4352 MiB (before push)."""
+    MiB = 1 << 20
+    full, stream = oracle.kv_bytes(1, 8, 32768, 128, 2, 4, 1020)
+    scores = [random.Random(3).random() for _ in range(64)]
+    for policy, peak in (("after", 4480), ("before", 4352)):
+        ev, _ = oracle.select_lazy_layers(scores, 32, policy=policy)
+        acc = oracle.kv_accounting(ev, full, stream, policy=policy, emit=True)
+        assert acc["retained"][-1] == 4352 * MiB
+        assert max(acc["transient"]) == peak * MiB
+        plain = oracle.kv_accounting(ev, full, stream, policy=policy)
+        # the difference is exactly one slice per layer still at full size
+        for l, (a, b) in enumerate(zip(acc["retained"], plain["retained"])):
+            n_full = (l + 1) - sum(1 for x in ev[:l + 1] if x >= 0)
+            assert a - b == n_full * stream
