@@ -271,7 +271,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // S^T for keys [32h, 32h+32) of a staged tile: s[kb][rb] holds keys
     // kb*16+4g+r of the step, query column c16.  The K fragments of 32-dim
-    // step ks+1 are read while the products of step ks run (the scheduling
+    // step ks+2 are read while the products of step ks run (the scheduling
     // groups fix that order).
     auto qk = [&](const bf16 *Kb, int h, f32x4 (&s)[NKB][RB]) {
 #pragma unroll
@@ -295,15 +295,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     s[kb][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[ks][kb], qreg[rb][ks],
                                                                         s[kb][rb], 0, 0, 0);
         // Scheduling groups (0x100: LDS reads, 0x008: matrix-core ops).
-        __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKB, 0);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + 1 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
+            if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, NKB, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, NKB * RB, 0);
         }
     };
     // O^T += V^T P^T for keys [32h, 32h+32) of a staged V tile; the V^T
-    // fragments of block db+2 are read while the products of block db run.
+    // fragments of block db+3 are read while the products of block db run.
     auto pv = [&](const bf16 *Vb, int h, const bf16x8 (&pk)[RB], f32x4 (&o)[RB][DB]) {
         const int row1 = BN * h + 4 * g + (c16 >> 2), row2 = row1 + 16;
         const int half = (c16 & 1) * 4;
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
                 o[rb][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[db], pk[rb], o[rb][db], 0, 0, 0);
-        constexpr int AHEAD = 2;  // 16-dim blocks whose V^T reads are in flight
+        constexpr int AHEAD = 3;  // 16-dim blocks whose V^T reads are in flight
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * AHEAD, 0);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
