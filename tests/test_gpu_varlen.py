@@ -181,3 +181,42 @@ def test_append_varlen_bit_exact():
             want_k[b, :, sl] = kn[b]
             want_v[b, :, sl] = vn[b]
     assert torch.equal(ks.cpu(), want_k) and torch.equal(vs.cpu(), want_v)
+
+
+def test_decode_varlen_graph_replay_with_new_lengths():
+    """One captured HIP graph of the varlen decode, replayed after writing new
+    lengths into the device array: every replay matches the oracle at its
+    lengths (eager work and a synchronisation between replays)."""
+    Hq, Hkv, D, L = 10, 2, 128, 3000
+    B = 4
+    g = torch.Generator().manual_seed(49)
+    q = torch.randn(B, Hq, D, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, L, D, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, L, D, generator=g).to(torch.bfloat16)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    lens = torch.tensor([L] * B, device=DEV, dtype=torch.int32)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, L, DEV)
+    out = torch.empty_like(qd)
+    lse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        api.lt_hybrid_decode_attn_varlen(qd, kd, vd, lens, L, out, lse, ws, 0.0, s)   # warm call
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        api.lt_hybrid_decode_attn_varlen(qd, kd, vd, lens, L, out, lse, ws, 0.0, s)
+    torch.cuda.synchronize()
+    for new in ([3000, 1, 1500, 0], [17, 2999, 64, 2048], [1, 1, 1, 3000]):
+        lens.copy_(torch.tensor(new, dtype=torch.int32))       # eager, outside the graph
+        _ = (qd.float() * 2.0).sum()                           # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = oracle.decode_varlen(np64(q), np64(k), np64(v), new)
+        for b, n in enumerate(new):
+            if n == 0:
+                assert (np64(out[b]) == 0).all() and (np64(lse[b]) == -np.inf).all()
+                continue
+            assert_close(f"replay {new} out b{b}", np64(out[b]), ref["out"][b], TOL_BF16_OUT)
+            assert_close(f"replay {new} lse b{b}", np64(lse[b]), ref["lse"][b], TOL_BF16_LSE)
