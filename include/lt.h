@@ -111,8 +111,10 @@ int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt
                       float *lse, int S, int R, hipStream_t stream);
 
 /*
- * Workspace for lt_hybrid_decode_attn at these sizes, in bytes (0 is
- * possible).  Host-only; no device call.
+ * Workspace for lt_hybrid_decode_attn at these sizes, in bytes: the split
+ * partial states, (parts + B - 1) * Hq * (D + 2) fp32.  The same size also
+ * serves lt_hybrid_decode_attn_varlen with max_kv_len = kv_len.  Host-only;
+ * no device call.  Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE (D).
  */
 int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len,
                                      size_t *bytes);

@@ -3,16 +3,22 @@
 // paragraph; press-release page, results) is what this step reads, so it is
 // bound by HBM bandwidth.
 //
-// Split-KV over equal parts of the batch: for each KV head the contexts of
-// the B sequences are laid end to end (T keys in all) and cut into P parts
-// of Q = ceil(T/P) keys.  Workgroup (kv head, part) streams its part once --
-// a segment of one sequence, or the end of one and the start of the next --
+// Split-KV.  Every workgroup streams a stretch of one KV head's keys once
 // and serves all G query heads of the group from each K/V row, keeping one
-// online-softmax state per head and writing one partial state per segment.
-// Every workgroup gets the same number of keys whatever the per-sequence
-// lengths are.  A second kernel merges each sequence's partial states with
-// their log-sum-exps.  The lengths may live on the device (kv_lens), so the
-// partition is computed there, by every workgroup, from them.
+// online-softmax state per head and writing one partial state per segment;
+// a second kernel merges each sequence's partial states with their
+// log-sum-exps.  Two ways of cutting the keys:
+//   * every context kv_len long: each sequence's keys are cut into `splits`
+//     splits of a multiple of 64 keys, one workgroup per (split, sequence,
+//     KV head) -- no partition arithmetic in the kernel;
+//   * per-sequence contexts (kv_lens, on the device): for each KV head the B
+//     contexts are laid end to end (T keys in all) and cut into P equal parts
+//     of Q = ceil(T/P) keys, one workgroup per (part, KV head), a part being
+//     a segment of one sequence or the end of one and the start of the next.
+//     Every workgroup gets the same number of keys whatever the length mix
+//     is; the partition is computed by every workgroup from the lengths.
+// Both write the partial of (sequence b, split or part p) to slot p + b (p
+// counted over the batch), so one merge kernel serves both.
 //
 // bf16 path (matrix cores, v_mfma_f32_16x16x32_bf16 for Q.K and P.V):
 //   S^T (16 keys x 16 columns) = K Q^T, where column c < G is query head
