@@ -189,6 +189,8 @@ def main(argv: Optional[List[str]] = None) -> int:
     ap.add_argument("--layers", type=int, default=None)
     ap.add_argument("--evict-before-push", action="store_true",
                     help="evict the laziest queued layer before pushing once the queue is full")
+    ap.add_argument("--emit-slices", action="store_true",
+                    help="each layer's prefill writes its streaming slice (no compaction on eviction)")
     ap.add_argument("--offline", type=int, default=0, metavar="P",
                     help="offline selection over P synthetic prompts instead of the test-time queue")
     args = ap.parse_args(argv)
@@ -223,7 +225,7 @@ def main(argv: Optional[List[str]] = None) -> int:
     print(f"[driver] {L} layers of B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D}, capacity {C}",
           file=sys.stderr, flush=True)
     policy = LT_EVICT_BEFORE_PUSH if args.evict_before_push else LT_EVICT_AFTER_PUSH
-    res = run(inputs, L, C, w.S, w.R, w.W, timing=True, policy=policy)
+    res = run(inputs, L, C, w.S, w.R, w.W, timing=True, policy=policy, emit=args.emit_slices)
     srt = sorted(res.layer_score)
     gaps = [b - a for a, b in zip(srt, srt[1:])]
     MiB = 1 << 20
@@ -232,6 +234,7 @@ def main(argv: Optional[List[str]] = None) -> int:
         "workload": f"driver64: {L} layers, B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D} bf16, "
                     f"S{w.S} R{w.R} W{w.W}, capacity {C}",
         "eviction": "before push" if args.evict_before_push else "after push",
+        "streaming_slices": "written by each prefill" if args.emit_slices else "compacted on eviction",
         "streaming_layers": [l for l in range(L) if res.is_streaming[l]],
         "full_layers": [l for l in range(L) if not res.is_streaming[l]],
         "evicted_at_step": res.evicted_at_step,
