@@ -189,9 +189,9 @@ def lt_prefill_attn_lse_lazy_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
         if t.dim() != 4 or t.shape[0] != B or t.shape[1] != k.shape[1] or t.shape[2] < min(N, S + R) \
                 or t.shape[3] != D:
             raise ValueError("streaming cache must be [B, Hkv, >= min(N, S+R), D]")
-    lens = 0 if seq_lens is None else _lens(seq_lens, B, "seq_lens")
+    lens = None if seq_lens is None else _lens(seq_lens, B, "seq_lens")
     shp = _shape(q, k, scale)
-    check(lib().lt_prefill_attn_lse_lazy_emit(ctypes.byref(shp), lens or None, _view(q), _view(k), _view(v),
+    check(lib().lt_prefill_attn_lse_lazy_emit(ctypes.byref(shp), lens, _view(q), _view(k), _view(v),
                                               _view(out), _ptr(lse), S, R, W, _ptr(lazy_rows), _ptr(lazy_ratio),
                                               _view(k_stream), _view(v_stream), _stream(stream)))
 
