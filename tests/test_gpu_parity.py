@@ -226,3 +226,48 @@ def test_prefill_emits_streaming_slice(B, N, Hq, Hkv, D, dtype, S, R, W, lens, s
         keep = oracle.streaming_rows(n, S, R)
         assert torch.equal(ksh[b, :, :len(keep)], kh[b, :, keep]) and torch.equal(vsh[b, :, :len(keep)], vh[b, :, keep])
         assert (ksh[b, :, len(keep):] == 7.0).all() and (vsh[b, :, len(keep):] == 7.0).all()
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_permuted_views_match_contiguous(dtype):
+    """Tensors stored as [B, N, H, D] (row stride H*D, head stride D) and passed
+    as permuted [B, H, N, D] views: prefill + lazy, streaming, the emitted
+    slice, compaction and decode give the contiguous calls' bits (the same
+    arithmetic at other addresses; the contiguous results are checked
+    against the oracle elsewhere)."""
+    from kv_cache_compression_causal_amd import api
+    B, N, Hq, Hkv, D, S, R, W = 2, 300, 10, 2, 128, 4, 60, 32
+    print(f"permuted views {dtype}", flush=True)
+    q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, 61, dtype))
+    qp = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)   # storage [B, N, Hq, D]
+    kp = k.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    vp = v.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert qp.stride(2) == Hq * D and qp.stride(1) == D and qp.shape == q.shape
+    ref = ops.prefill(q, k, v, S, R, W)
+    out_p = torch.empty(B, N, Hq, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    lse = torch.empty(B, Hq, N, device=DEV, dtype=torch.float32)
+    rows = torch.empty(B, Hq, W, device=DEV, dtype=torch.float32)
+    ratio = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    ks_p = torch.empty(B, S + R, Hkv, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    vs_p = torch.empty_like(ks_p.permute(0, 2, 1, 3)).permute(0, 2, 1, 3)
+    api.lt_prefill_attn_lse_lazy_emit(qp, kp, vp, out_p, lse, S, R, W, rows, ratio, ks_p, vs_p)
+    sref = ops.streaming(q, k, v, S, R)
+    sout_p = torch.empty(B, N, Hq, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    slse = torch.empty(B, Hq, N, device=DEV, dtype=torch.float32)
+    api.lt_streaming_attn(qp, kp, vp, sout_p, slse, S, R)
+    cks, cvs = ops.compact(k, v, S, R)
+    cks_p = torch.empty(B, S + R, Hkv, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    cvs_p = torch.empty(B, S + R, Hkv, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    api.lt_compact_kv_streaming(kp, vp, cks_p, cvs_p, S, R)
+    qd = q[:, :, N - 1].contiguous()
+    dref = ops.decode(qd, k, v)
+    dout = torch.empty_like(qd)
+    dlse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    api.lt_hybrid_decode_attn(qd, kp, vp, N, dout, dlse, ops.decode_workspace(B, Hq, Hkv, D, N, DEV))
+    torch.cuda.synchronize()
+    assert torch.equal(out_p, ref[0]) and torch.equal(lse, ref[1])
+    assert torch.equal(rows, ref[2]) and torch.equal(ratio, ref[3])
+    assert torch.equal(sout_p, sref[0]) and torch.equal(slse, sref[1])
+    assert torch.equal(ks_p, cks) and torch.equal(vs_p, cvs)
+    assert torch.equal(cks_p, cks) and torch.equal(cvs_p, cvs)
+    assert torch.equal(dout, dref[0]) and torch.equal(dlse, dref[1])
