@@ -32,7 +32,10 @@
  *   Views: lt_view.data is a DEVICE pointer; sb, sh, sn are element strides of
  *   the batch, head and row dims; the head dim is contiguous.  Data pointers
  *   must be 16-byte aligned and strides multiples of 8 elements (bf16) or 4
- *   (f32), so 128-bit loads are legal.
+ *   (f32), so 128-bit loads are legal; a row stride sn may not exceed 2^25
+ *   elements (the attention kernels keep a lane's offset into a K/V tile in
+ *   32 bits).  Sizes: N * (Hq/Hkv) must stay below 2^31 - 4096 and
+ *   B * Hq * N at or below 2^38 (LT_ERR_SHAPE otherwise).
  *   Ownership: the caller owns every buffer (device memory and workspace);
  *   the library never allocates or frees device memory.
  *   Streams: device calls are asynchronous on the given stream, never

@@ -34,6 +34,8 @@ int elem_size(int dtype) { return dtype == LT_BF16 ? 2 : dtype == LT_F32 ? 4 : 0
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int64_t kMaxRowStride = (int64_t)1 << 25;
+
 // A [B, H, rows, D] view: pointer, alignment and stride checks.
 int check_view(const lt_view &v, const char *name, int dtype) {
     if (v.data == nullptr) return fail(LT_ERR_NULL, "%s.data is NULL", name);
@@ -42,6 +44,10 @@ int check_view(const lt_view &v, const char *name, int dtype) {
     if (v.sb < 0 || v.sh < 0 || v.sn < 0 || v.sb % m || v.sh % m || v.sn % m)
         return fail(LT_ERR_LAYOUT, "%s strides (%lld, %lld, %lld) must be non-negative multiples of %lld",
                     name, (long long)v.sb, (long long)v.sh, (long long)v.sn, (long long)m);
+    // A lane's byte offset into a K/V tile (up to 64 rows) is kept in 32 bits.
+    if (v.sn > kMaxRowStride)
+        return fail(LT_ERR_LAYOUT, "%s row stride %lld exceeds %lld elements", name, (long long)v.sn,
+                    (long long)kMaxRowStride);
     return LT_OK;
 }
 
@@ -53,6 +59,11 @@ int check_shape(const lt_shape *s) {
         return fail(LT_ERR_SHAPE, "B, N, Hq, Hkv must be >= 1 (got %d, %d, %d, %d)", s->B, s->N, s->Hq, s->Hkv);
     if (s->Hq % s->Hkv != 0) return fail(LT_ERR_SHAPE, "Hq %d is not a multiple of Hkv %d", s->Hq, s->Hkv);
     if ((int64_t)s->N * 64 > INT32_MAX) return fail(LT_ERR_SHAPE, "N %d too large", s->N);
+    // Flattened rows (position * group size + head) are int, and so is the
+    // workgroup count (about B * Hq * N / 384).
+    if ((int64_t)s->N * (s->Hq / s->Hkv) > INT32_MAX - 4096 || (int64_t)s->B * s->Hq * s->N > ((int64_t)1 << 38))
+        return fail(LT_ERR_SHAPE, "N * Hq/Hkv or B * Hq * N too large (B=%d, N=%d, Hq=%d, Hkv=%d)", s->B, s->N,
+                    s->Hq, s->Hkv);
     if (!(s->scale == s->scale) || isinf(s->scale)) return fail(LT_ERR_VALUE, "scale is not finite");
     return LT_OK;
 }

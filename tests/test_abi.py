@@ -70,6 +70,8 @@ def prefill(L, shp, q=None, k=None, v=None, o=None, lse=GOOD, S=4, R=8, W=4, row
     (dict(B=0), _lib.LT_ERR_SHAPE),
     (dict(scale=float("nan")), _lib.LT_ERR_VALUE),
     (dict(scale=float("inf")), _lib.LT_ERR_VALUE),
+    (dict(N=1 << 24, Hq=256, Hkv=1), _lib.LT_ERR_SHAPE),    # N * group size overflows int
+    (dict(B=1 << 14, N=1 << 20, Hq=32), _lib.LT_ERR_SHAPE),  # B * Hq * N > 2^38
 ])
 def test_prefill_shape_errors(L, kw, code):
     assert prefill(L, shape(**kw)) == code
@@ -83,6 +85,8 @@ def test_prefill_argument_errors(L):
     assert prefill(L, s, k=view(ptr=GOOD + 2)) == _lib.LT_ERR_LAYOUT
     assert prefill(L, s, v=view(sn=130)) == _lib.LT_ERR_LAYOUT
     assert prefill(L, s, o=view(sb=-8)) == _lib.LT_ERR_LAYOUT
+    assert prefill(L, s, k=view(sn=(1 << 25) + 8)) == _lib.LT_ERR_LAYOUT  # row stride limit
+    assert prefill(L, s, k=view(sn=1 << 25), R=0) == _lib.LT_ERR_SHAPE    # at the limit: accepted
     assert prefill(L, s, lse=None) == _lib.LT_ERR_NULL
     assert prefill(L, s, W=65) == _lib.LT_ERR_SHAPE
     assert prefill(L, s, W=-1) == _lib.LT_ERR_SHAPE
