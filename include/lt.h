@@ -28,7 +28,8 @@
  *   position 0: key j is visible to query i iff j <= i), Hq query heads, Hkv
  *   KV heads with Hq % Hkv == 0 (query head h reads KV head h / (Hq/Hkv)),
  *   D head dim (64 or 128).  The recent set of query i is (i-R, i], the sink
- *   set [0, S).
+ *   set [0, S); every call that takes them needs S >= 0, R >= 1 and
+ *   S + R <= 2^30 (LT_ERR_SHAPE otherwise).
  *   Views: lt_view.data is a DEVICE pointer; sb, sh, sn are element strides of
  *   the batch, head and row dims; the head dim is contiguous.  Data pointers
  *   must be 16-byte aligned and strides multiples of 8 elements (bf16) or 4

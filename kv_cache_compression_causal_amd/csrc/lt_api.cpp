@@ -36,6 +36,9 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int64_t kMaxRowStride = (int64_t)1 << 25;
 
+// Sink + recent window: S + R and i - R stay far inside int.
+bool window_ok(int S, int R) { return (int64_t)S + R <= ((int64_t)1 << 30); }
+
 // A [B, H, rows, D] view: pointer, alignment and stride checks.
 int check_view(const lt_view &v, const char *name, int dtype) {
     if (v.data == nullptr) return fail(LT_ERR_NULL, "%s.data is NULL", name);
@@ -99,7 +102,8 @@ int prefill(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt
         (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
         return e;
     if (lse == nullptr) return fail(LT_ERR_NULL, "lse is NULL");
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    if (S < 0 || R < 1 || !window_ok(S, R))
+        return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, S + R <= 2^30 (got S=%d, R=%d)", S, R);
     if (W < 0 || W > shape->N) return fail(LT_ERR_SHAPE, "W %d outside [0, N=%d]", W, shape->N);
     if (W > 0 && (lazy_rows == nullptr || lazy_ratio == nullptr))
         return fail(LT_ERR_NULL, "W > 0 needs lazy_rows and lazy_ratio");
@@ -129,7 +133,8 @@ int streaming(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, 
     if ((e = check_view(q, "q", shape->dtype)) || (e = check_view(k, "k", shape->dtype)) ||
         (e = check_view(v, "v", shape->dtype)) || (e = check_view(out, "out", shape->dtype)))
         return e;
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1 (got S=%d, R=%d)", S, R);
+    if (S < 0 || R < 1 || !window_ok(S, R))
+        return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, S + R <= 2^30 (got S=%d, R=%d)", S, R);
     lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, 0, nullptr);
     a.seq_len = lens;
     hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, lt::MODE_STREAM, stream)
@@ -191,7 +196,7 @@ int compact(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, 
     if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
     if (B < 1 || Hkv < 1 || N < 1) return fail(LT_ERR_SHAPE, "B, Hkv, N must be >= 1");
-    if (S < 0 || R < 1) return fail(LT_ERR_SHAPE, "need S >= 0 and R >= 1");
+    if (S < 0 || R < 1 || !window_ok(S, R)) return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, S + R <= 2^30");
     int e;
     if ((e = check_view(k_full, "k_full", dtype)) || (e = check_view(v_full, "v_full", dtype)) ||
         (e = check_view(k_stream, "k_stream", dtype)) || (e = check_view(v_stream, "v_stream", dtype)))
@@ -213,7 +218,8 @@ int append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_
     if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
     if (B < 1 || Hkv < 1) return fail(LT_ERR_SHAPE, "B and Hkv must be >= 1");
-    if (S < 0 || R < 1 || pos < 0) return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, pos >= 0");
+    if (S < 0 || R < 1 || pos < 0 || !window_ok(S, R))
+        return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, S + R <= 2^30, pos >= 0");
     if (k_new == nullptr || v_new == nullptr) return fail(LT_ERR_NULL, "k_new/v_new is NULL");
     if (!aligned16(k_new) || !aligned16(v_new)) return fail(LT_ERR_LAYOUT, "k_new/v_new not 16-byte aligned");
     int e;

@@ -92,6 +92,8 @@ def test_prefill_argument_errors(L):
     assert prefill(L, s, W=-1) == _lib.LT_ERR_SHAPE
     assert prefill(L, s, R=0) == _lib.LT_ERR_SHAPE
     assert prefill(L, s, S=-1) == _lib.LT_ERR_SHAPE
+    assert prefill(L, s, S=1 << 30, R=1) == _lib.LT_ERR_SHAPE   # S + R past 2^30
+    assert prefill(L, s, S=(1 << 30) - 1, R=1, rows=None) == _lib.LT_ERR_NULL  # at the limit: accepted
     assert prefill(L, s, rows=None) == _lib.LT_ERR_NULL
     assert prefill(L, s, ratio=None) == _lib.LT_ERR_NULL
     # fp32 allows strides that are multiples of 4 elements
