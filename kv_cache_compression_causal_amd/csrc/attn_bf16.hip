@@ -141,11 +141,12 @@ __device__ __forceinline__ int swz_v(int row, int chunk) {
 
 // Work decomposition: the queries of one (batch, KV head) are flattened
 // position-major over the G query heads of the group, r = position * G +
-// head-in-group.  A workgroup of NW = 8 waves (two per SIMD) owns NW*16*RB
-// consecutive rows r; each wave owns RB row blocks of 16.  K/V tiles of BT
-// keys are staged in LDS once per workgroup and read by every wave, so the
-// whole GQA group shares each tile; inside a wave each K fragment read from
-// LDS feeds RB matrix-core ops.  The causal mask uses each lane's own
+// head-in-group.  A workgroup of NW waves (8 for full attention, one
+// workgroup and two waves per SIMD; 4 for streaming, two workgroups per CU)
+// owns NW*16*RB consecutive rows r; each wave owns RB row blocks of 16.  K/V
+// tiles of BT keys are staged in LDS once per workgroup and read by every
+// wave, so the whole GQA group shares each tile; inside a wave each K fragment
+// read from LDS feeds RB matrix-core ops.  The causal mask uses each lane's own
 // position, so rows of different heads and positions mix freely inside a
 // row block.  While one wave of a SIMD runs its softmax or waits on LDS, the
 // other wave's matrix-core products run.
@@ -389,9 +390,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int h = 0; h < NH; ++h) {
             const int key0 = tile_of(it) * BT + BN * h;
             if (key0 > w_last) continue;  // every key of the step is in this wave's future
+            // Streaming: a step of non-sink keys below every row's window adds
+            // nothing (its weights would all be zero) and is skipped.
+            if (MODE == MODE_STREAM && key0 >= a.S && key0 + BN - 1 <= w_first - a.R) continue;
             f32x4 s[NKB][RB];
             qk(Kb, h, s);
-            const bool masked = (MODE == MODE_STREAM) || (key0 + BN - 1 > w_first);
+            // Steps whose every key every row sees run unmasked: under the
+            // diagonal and, for streaming, all sinks or all inside the window
+            // of the wave's last row (hence of every row).
+            const bool masked = (MODE == MODE_STREAM)
+                ? !((key0 + BN - 1 <= w_first) & ((key0 + BN - 1 < a.S) | (key0 > w_last - a.R)))
+                : (key0 + BN - 1 > w_first);
             if (masked) mask(s, key0);
             // Online softmax in log2 units.  Weights are taken against the
             // running reference max m of each row, which is allowed to lag the
@@ -589,9 +598,13 @@ template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
     // 3 row blocks per wave: O (3*D/16 x 4), S^T (3 x 8), Q^T (3*D/16 x 2)
     // and the rest fit 256 registers for two waves per SIMD.  Full attention
-    // takes 128-key tiles (half the workgroup barriers per key); streaming,
-    // which keeps its raw scores, stays at 64 keys to fit its registers.
-    if (mode == MODE_STREAM) return launch_cfg<D, 3, 64, 8, 1 << MODE_STREAM>(a, mode, st);
+    // takes 128-key tiles (half the workgroup barriers per key) in 8-wave
+    // workgroups, one per CU.  Streaming, which keeps its raw scores, stays at
+    // 64 keys to fit its registers, in 4-wave workgroups: a window of about
+    // S + R keys is short work next to the workgroup's own Q loads and O
+    // stores, and with two workgroups per CU one computes while the other
+    // waits on memory.
+    if (mode == MODE_STREAM) return launch_cfg<D, 3, 64, 4, 1 << MODE_STREAM>(a, mode, st);
     return launch_cfg<D, 3, 128, 8, (1 << MODE_FULL) | (1 << MODE_FULL_LAZY)>(a, mode, st);
 }
 
