@@ -92,7 +92,8 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the kernels run on one GPU's share; see DESIGN.md for how it would shard).",
+              "(the kernels run on one GPU's share: the (batch, KV head) units a multi-GPU run "
+              "would spread over its GPUs).",
               file=sys.stderr)
         return 2
 

@@ -23,7 +23,7 @@ Sources (LightTransfer web pages; cited by page title and section):
     sums the attention weights from queries to the initial and recent keys;
     offline, the 50% of layers with the highest ratio are replaced.
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
   * the queue pushes first and pops while its size exceeds the capacity, so
     the current layer can be evicted at its own step; equal scores evict the
     lower layer index first;

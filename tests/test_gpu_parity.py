@@ -71,6 +71,12 @@ STREAM_CASES = [
     (1, 200, 4, 2, 64, torch.bfloat16, 70, 1, 5),      # R = 1: sinks + diagonal
     (1, 100, 16, 2, 128, torch.bfloat16, 4, 200, 6),   # S + R >= N: full attention
     (1, 257, 6, 2, 128, torch.float32, 3, 64, 7),
+    # long windows: steps wholly inside every row's window run unmasked, and
+    # non-sink steps below every window are skipped
+    (1, 900, 2, 2, 128, torch.bfloat16, 4, 300, 8),    # G=1
+    (1, 700, 16, 2, 128, torch.bfloat16, 5, 250, 9),   # G=8
+    (1, 640, 4, 2, 64, torch.bfloat16, 33, 150, 10),   # a step of sinks only, then a mixed one
+    (1, 800, 5, 1, 128, torch.bfloat16, 64, 128, 11),  # two whole sink steps
 ]
 
 
