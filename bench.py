@@ -91,7 +91,7 @@ def main() -> int:
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the kernels run on one GPU's share: the (batch, KV head) units a multi-GPU run "
               "would spread over its GPUs).",
               file=sys.stderr)
