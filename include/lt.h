@@ -323,8 +323,10 @@ int lt_select_offline(const float *head_ratio, int P, int L, int n, int C, doubl
  * `stream`; the caller times them (e.g. with events on that stream).
  *   lt_probe_mfma_bf16: `blocks` workgroups of 4 waves; each wave runs
  *     `iters` rounds of 8 independent 16x16x32 bf16 matrix-core products
- *     (16384 FLOP each), i.e. blocks*4*iters*8*16384 FLOP.  sink: device
- *     fp32 [blocks*256], overwritten with meaningless values.
+ *     (16384 FLOP each), i.e. blocks*4*iters*8*16384 FLOP, on pseudo-random
+ *     register operands of unit size (the sustained rate depends on the
+ *     data; constant operands run faster).  sink: device fp32
+ *     [blocks*256], overwritten with meaningless values.
  *   lt_probe_read: reads `bytes` of device memory at `buf` once (16-byte
  *     aligned, bytes a multiple of 16) with `blocks` workgroups of 256
  *     lanes.  sink: device u32 [blocks], written only on an unlikely value.

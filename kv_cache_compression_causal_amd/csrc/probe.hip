@@ -4,7 +4,11 @@
 //
 // mfma_probe_kernel: every wave runs 8 independent accumulator chains of
 // v_mfma_f32_16x16x32_bf16 on register operands (each product depends on the
-// previous one of its chain, so nothing can be hoisted out of the loop).
+// previous one of its chain, so nothing can be hoisted out of the loop).  The
+// operands are pseudo-random values of unit size, different in every lane and
+// chain: the rate the matrix cores hold depends on the data (their switching
+// power sets the clock), and constant or small-integer operands run faster
+// than attention's inputs do.
 // read_probe_kernel: each workgroup streams its contiguous share with 16-byte
 // loads, 16 in flight per lane, folded with xor so the loads are live.
 #include "lt_internal.h"
@@ -14,26 +18,34 @@ namespace {
 
 // (No launch bounds: with them the compiler put the accumulators in AGPRs and
 // moved them around every iteration.)
+// A value in [-2, 2) from an integer (an integer hash, then scaled).
+__device__ __forceinline__ float probe_value(unsigned x) {
+    x ^= x >> 16;
+    x *= 0x7feb352du;
+    x ^= x >> 15;
+    x *= 0x846ca68bu;
+    x ^= x >> 16;
+    return (float)(x & 0xffffu) * (1.f / 16384.f) - 2.f;
+}
+
 __global__ void mfma_probe_kernel(int iters, float *sink) {
     const int t = threadIdx.x;
-    bf16x8 a, b;
+    const unsigned id = blockIdx.x * 256u + (unsigned)t;
+    bf16x8 a[8], b;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a[e] = (bf16)(0.001f * (float)((t + e) & 31));
-        b[e] = (bf16)(0.002f * (float)((t * 3 + e) & 15));
-    }
-    f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = c0, c2 = c0, c3 = c0, c4 = c0, c5 = c0, c6 = c0, c7 = c0;
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[i][e] = (bf16)probe_value(id * 97u + e * 13u + i * 1001u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) b[e] = (bf16)probe_value(id * 31u + e * 7u + 55555u);
+    f32x4 c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it) {
-        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c1, 0, 0, 0);
-        c2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c2, 0, 0, 0);
-        c3 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c3, 0, 0, 0);
-        c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c4, 0, 0, 0);
-        c5 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c5, 0, 0, 0);
-        c6 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c6, 0, 0, 0);
-        c7 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c7, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b, c[i], 0, 0, 0);
     }
-    const f32x4 cs = c0 + c1 + c2 + c3 + c4 + c5 + c6 + c7;
+    const f32x4 cs = c[0] + c[1] + c[2] + c[3] + c[4] + c[5] + c[6] + c[7];
     const float acc = cs[0] + cs[1] + cs[2] + cs[3];
     sink[(size_t)blockIdx.x * 256 + t] = acc;
 }
