@@ -23,17 +23,27 @@ def _dtype_code(t: torch.Tensor) -> int:
     return _DTYPES[t.dtype]
 
 
+def _dev(t: torch.Tensor) -> int:
+    """Device address of a tensor on the current GPU (the kernels run there:
+    a host or other-device pointer would fault instead of failing)."""
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the GPU")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"tensor on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    return t.data_ptr()
+
+
 def _view(t: torch.Tensor) -> LtView:
     """[B, H, rows, D] tensor -> lt_view (head dim must be contiguous)."""
     if t.dim() != 4:
         raise ValueError("expected a [B, H, rows, D] tensor")
     if t.stride(3) != 1:
         raise ValueError("head dim must be contiguous")
-    return LtView(t.data_ptr(), t.stride(0), t.stride(1), t.stride(2))
+    return LtView(_dev(t), t.stride(0), t.stride(1), t.stride(2))
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    return None if t is None else _dev(t)
 
 
 def _stream(stream) -> Optional[int]:
@@ -54,6 +64,19 @@ def _same_dtype(*ts: torch.Tensor) -> None:
         raise TypeError("q, k, v and out must share one dtype")
 
 
+def _lazy_outputs(rows: Optional[torch.Tensor], ratio: Optional[torch.Tensor], B: int, Hq: int, W: int):
+    """With W > 0 the kernels write rows [B, Hq, W] and ratio [B, Hq] (fp32,
+    contiguous); W == 0 writes neither, and both are passed as NULL."""
+    if W <= 0:
+        return None, None
+    for t, shape, name in ((rows, (B, Hq, W), "lazy_rows"), (ratio, (B, Hq), "lazy_ratio")):
+        if t is None:
+            continue  # the library reports the missing buffer
+        if t.dtype != torch.float32 or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a contiguous float32 {list(shape)} tensor")
+    return _ptr(rows), _ptr(ratio)
+
+
 def lt_prefill_attn_lse_lazy(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
                              lse: torch.Tensor, S: int, R: int, W: int,
                              lazy_rows: Optional[torch.Tensor] = None,
@@ -65,9 +88,9 @@ def lt_prefill_attn_lse_lazy(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
     shp = _shape(q, k, scale)
+    rows, ratio = _lazy_outputs(lazy_rows, lazy_ratio, q.shape[0], q.shape[1], W)
     check(lib().lt_prefill_attn_lse_lazy(ctypes.byref(shp), _view(q), _view(k), _view(v), _view(out),
-                                         _ptr(lse), S, R, W, _ptr(lazy_rows), _ptr(lazy_ratio),
-                                         _stream(stream)))
+                                         _ptr(lse), S, R, W, rows, ratio, _stream(stream)))
 
 
 def lt_streaming_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
@@ -107,8 +130,8 @@ def lt_hybrid_decode_attn(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
                             or tuple(lse.shape) != (B, Hq)):
         raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
     check(lib().lt_hybrid_decode_attn(B, Hq, k_cache.shape[1], D, _dtype_code(q), float(scale),
-                                      q.data_ptr(), _view(k_cache), _view(v_cache), int(kv_len),
-                                      out.data_ptr(), _ptr(lse), ws.data_ptr(),
+                                      _ptr(q), _view(k_cache), _view(v_cache), int(kv_len),
+                                      _ptr(out), _ptr(lse), _ptr(ws),
                                       ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -141,8 +164,8 @@ def lt_stream_cache_append(k_stream: torch.Tensor, v_stream: torch.Tensor, k_new
     if rows < min(pos + 1, S + R):
         raise ValueError("streaming cache has too few rows for this position")
     _same_dtype(k_stream, v_stream, k_new, v_new)
-    check(lib().lt_stream_cache_append(_view(k_stream), _view(v_stream), k_new.data_ptr(),
-                                       v_new.data_ptr(), B, Hkv, D, _dtype_code(k_stream), S, R,
+    check(lib().lt_stream_cache_append(_view(k_stream), _view(v_stream), _ptr(k_new),
+                                       _ptr(v_new), B, Hkv, D, _dtype_code(k_stream), S, R,
                                        int(pos), _stream(stream)))
 
 
@@ -150,7 +173,7 @@ def _lens(t: torch.Tensor, B: int, name: str) -> int:
     """Per-sequence length / position array: a contiguous int32 [B] device tensor."""
     if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != B or not t.is_contiguous() or not t.is_cuda:
         raise ValueError(f"{name} must be a contiguous int32 [B] device tensor")
-    return t.data_ptr()
+    return _dev(t)
 
 
 def lt_prefill_attn_lse_lazy_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
@@ -166,9 +189,10 @@ def lt_prefill_attn_lse_lazy_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.T
     if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != tuple(q.shape[:3]):
         raise ValueError("lse must be a contiguous float32 [B, Hq, N] tensor")
     shp = _shape(q, k, scale)
+    rows, ratio = _lazy_outputs(lazy_rows, lazy_ratio, q.shape[0], q.shape[1], W)
     check(lib().lt_prefill_attn_lse_lazy_varlen(ctypes.byref(shp), _lens(seq_lens, q.shape[0], "seq_lens"),
                                                 _view(q), _view(k), _view(v), _view(out), _ptr(lse), S, R,
-                                                W, _ptr(lazy_rows), _ptr(lazy_ratio), _stream(stream)))
+                                                W, rows, ratio, _stream(stream)))
 
 
 def lt_prefill_attn_lse_lazy_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
@@ -191,8 +215,9 @@ def lt_prefill_attn_lse_lazy_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Ten
             raise ValueError("streaming cache must be [B, Hkv, >= min(N, S+R), D]")
     lens = None if seq_lens is None else _lens(seq_lens, B, "seq_lens")
     shp = _shape(q, k, scale)
+    rows, ratio = _lazy_outputs(lazy_rows, lazy_ratio, B, Hq, W)
     check(lib().lt_prefill_attn_lse_lazy_emit(ctypes.byref(shp), lens, _view(q), _view(k), _view(v),
-                                              _view(out), _ptr(lse), S, R, W, _ptr(lazy_rows), _ptr(lazy_ratio),
+                                              _view(out), _ptr(lse), S, R, W, rows, ratio,
                                               _view(k_stream), _view(v_stream), _stream(stream)))
 
 
@@ -228,9 +253,9 @@ def lt_hybrid_decode_attn_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache
                             or tuple(lse.shape) != (B, Hq)):
         raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
     check(lib().lt_hybrid_decode_attn_varlen(B, Hq, k_cache.shape[1], D, _dtype_code(q), float(scale),
-                                             q.data_ptr(), _view(k_cache), _view(v_cache),
-                                             _lens(kv_lens, B, "kv_lens"), int(max_kv_len), out.data_ptr(),
-                                             _ptr(lse), ws.data_ptr(), ws.numel() * ws.element_size(),
+                                             _ptr(q), _view(k_cache), _view(v_cache),
+                                             _lens(kv_lens, B, "kv_lens"), int(max_kv_len), _ptr(out),
+                                             _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                              _stream(stream)))
 
 
@@ -264,8 +289,8 @@ def lt_stream_cache_append_varlen(k_stream: torch.Tensor, v_stream: torch.Tensor
     if rows < S + R:
         raise ValueError("the streaming cache needs S + R slots")
     _same_dtype(k_stream, v_stream, k_new, v_new)
-    check(lib().lt_stream_cache_append_varlen(_view(k_stream), _view(v_stream), k_new.data_ptr(),
-                                              v_new.data_ptr(), B, Hkv, D, _dtype_code(k_stream), S, R,
+    check(lib().lt_stream_cache_append_varlen(_view(k_stream), _view(v_stream), _ptr(k_new),
+                                              _ptr(v_new), B, Hkv, D, _dtype_code(k_stream), S, R,
                                               _lens(pos, B, "pos"), _stream(stream)))
 
 
@@ -352,7 +377,7 @@ def lt_probe_mfma_bf16(blocks: int, iters: int, sink: torch.Tensor, stream=None)
     times it).  sink: float32 device tensor of at least blocks*256 elements."""
     if sink.dtype != torch.float32 or sink.numel() < blocks * 256 or not sink.is_contiguous():
         raise ValueError("sink must be a contiguous float32 tensor of blocks*256 elements")
-    check(lib().lt_probe_mfma_bf16(int(blocks), int(iters), sink.data_ptr(), _stream(stream)))
+    check(lib().lt_probe_mfma_bf16(int(blocks), int(iters), _ptr(sink), _stream(stream)))
     return float(blocks) * 4 * iters * 8 * 16384
 
 
@@ -361,5 +386,5 @@ def lt_probe_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, stream=Non
     nbytes = buf.numel() * buf.element_size()
     if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < blocks:
         raise ValueError("buf must be contiguous; sink an int32 tensor of >= blocks elements")
-    check(lib().lt_probe_read(buf.data_ptr(), nbytes, int(blocks), sink.data_ptr(), _stream(stream)))
+    check(lib().lt_probe_read(_ptr(buf), nbytes, int(blocks), _ptr(sink), _stream(stream)))
     return nbytes

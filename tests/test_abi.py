@@ -12,6 +12,7 @@ import random
 import re
 
 import numpy as np
+import torch
 import pytest
 
 import oracle
@@ -312,3 +313,30 @@ def test_stream_append_errors(L):
     assert f(view(), view(), None, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_NULL
     assert f(view(), view(), GOOD + 8, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_LAYOUT
     assert f(view(ptr=GOOD + 8), view(), GOOD, GOOD, 2, 2, 128, bf, 4, 60, 10, None) == _lib.LT_ERR_LAYOUT
+
+
+def test_binding_refuses_host_tensors_and_bad_lazy_buffers():
+    """The Python binding checks, before any call, that tensors live on the
+    GPU (a host pointer reaching a kernel would fault) and that the lazy
+    outputs have the shapes the kernels write."""
+    from kv_cache_compression_causal_amd import api
+    B, Hq, Hkv, N, D, W = 1, 4, 2, 64, 128, 8
+    q = torch.zeros(B, Hq, N, D, dtype=torch.bfloat16)
+    k = torch.zeros(B, Hkv, N, D, dtype=torch.bfloat16)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(B, Hq, N)
+    rows, ratio = torch.zeros(B, Hq, W), torch.zeros(B, Hq)
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.lt_prefill_attn_lse_lazy(q, k, k, out, lse, 4, 8, W, rows, ratio)
+    with pytest.raises(ValueError, match="lazy_rows"):
+        api.lt_prefill_attn_lse_lazy(q, k, k, out, lse, 4, 8, W, torch.zeros(B, Hq, W - 1), ratio)
+    with pytest.raises(ValueError, match="lazy_ratio"):
+        api.lt_prefill_attn_lse_lazy(q, k, k, out, lse, 4, 8, W, rows, torch.zeros(B, Hq, dtype=torch.float64))
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.lt_streaming_attn(q, k, k, out, lse, 4, 8)
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.lt_hybrid_decode_attn(q[:, :, 0].contiguous(), k, k, N, out[:, :, 0].contiguous(), None,
+                                  torch.zeros(1 << 20, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="on the GPU"):
+        api.lt_compact_kv_streaming(k, k, torch.zeros(B, Hkv, 12, D, dtype=torch.bfloat16),
+                                    torch.zeros(B, Hkv, 12, D, dtype=torch.bfloat16), 4, 8)
