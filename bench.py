@@ -403,7 +403,7 @@ def main() -> int:
         "hbm_read_gbps": round(rbuf.numel() / (read_ms * 1e-3) / 1e9, 1),
         "spec_mfma_bf16_tflops": PEAK_BF16 / 1e12, "spec_hbm_gbps": PEAK_HBM / 1e9,
         "probes": "lt_probe_mfma_bf16: 2048 workgroups x 4 waves, 8 independent 16x16x32 bf16 "
-                  "MFMA chains per wave on pseudo-random unit-size register operands, 20000 iterations; lt_probe_read: one pass of 16-byte loads over 4 GiB (contiguous share per workgroup), "
+                  "MFMA chains per wave on pseudo-random unit-size register operands, 20000 iterations; lt_probe_read: one pass of 16-byte nontemporal loads over 4 GiB (contiguous share per workgroup), "
                   "8192 workgroups; best of 3"}
     log(f"measured peaks: {result['measured_peaks']['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
         f"{result['measured_peaks']['hbm_read_gbps']} GB/s read")

@@ -329,7 +329,7 @@ int lt_select_offline(const float *head_ratio, int P, int L, int n, int C, doubl
  *     [blocks*256], overwritten with meaningless values.
  *   lt_probe_read: reads `bytes` of device memory at `buf` once (16-byte
  *     aligned, bytes a multiple of 16) with `blocks` workgroups of 256
- *     lanes.  sink: device u32 [blocks], written only on an unlikely value.
+ *     lanes, in nontemporal 16-byte loads.  sink: device u32 [blocks], written only on an unlikely value.
  * Errors: LT_ERR_NULL (null pointer), LT_ERR_SHAPE (blocks < 1, iters < 1,
  * bytes not a positive multiple of 16), LT_ERR_LAYOUT (buf not 16-byte
  * aligned), LT_ERR_HIP (launch failure).
