@@ -42,6 +42,9 @@ PREFILL_CASES = [
     (333, 3, 3, 128, torch.bfloat16, 0, 50, 20, [333, 129, 128], 34),         # G=1, S=0
     (200, 8, 2, 128, torch.float32, 4, 60, 50, [200, 3, 120], 35),            # fp32
     (130, 6, 3, 64, torch.float32, 0, 7, 130, [130, 1, 64, 0], 36),           # fp32, W=N
+    # long windows: unmasked steps inside every row's window, skipped steps below it
+    (800, 8, 2, 128, torch.bfloat16, 4, 250, 32, [800, 640, 300, 33], 37),    # G=4
+    (700, 5, 1, 64, torch.bfloat16, 40, 180, 24, [700, 500, 41], 38),         # G=5, D=64, a step of sinks only
 ]
 
 
