@@ -54,8 +54,7 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16 *__restrict__ p) {
 // layout) stay plain: marked nontemporal, each row's lines were fetched
 // piecemeal and the kernel ran 15% slower.
 __device__ __forceinline__ bf16x8 load_stream(const bf16 *p) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-    return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load((const u32x4 *)p));
+    return __builtin_nontemporal_load((const bf16x8 *)p);
 }
 
 // V tiles in LDS use the same 16-byte-chunk swizzle as the prefill kernel,
