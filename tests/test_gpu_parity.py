@@ -277,3 +277,21 @@ def test_permuted_views_match_contiguous(dtype):
     assert torch.equal(ks_p, cks) and torch.equal(vs_p, cvs)
     assert torch.equal(cks_p, cks) and torch.equal(cvs_p, cvs)
     assert torch.equal(dout, dref[0]) and torch.equal(dlse, dref[1])
+    # the same views through the per-sequence-length calls
+    lens = [N, N // 3]
+    vref = ops.prefill_varlen(q, k, v, lens, S, R, W)
+    vout_p = torch.empty(B, N, Hq, D, device=DEV, dtype=dtype).permute(0, 2, 1, 3)
+    vlse = torch.empty(B, Hq, N, device=DEV, dtype=torch.float32)
+    vrows = torch.empty(B, Hq, W, device=DEV, dtype=torch.float32)
+    vratio = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    lens_d = torch.tensor(lens, device=DEV, dtype=torch.int32)
+    api.lt_prefill_attn_lse_lazy_varlen(qp, kp, vp, vout_p, vlse, lens_d, S, R, W, vrows, vratio)
+    kvref = ops.decode_varlen(qd, k, v, lens)
+    kvout = torch.empty_like(qd)
+    kvlse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    api.lt_hybrid_decode_attn_varlen(qd, kp, vp, lens_d, N, kvout, kvlse,
+                                     ops.decode_workspace(B, Hq, Hkv, D, N, DEV))
+    torch.cuda.synchronize()
+    for b, n in enumerate(lens):
+        assert torch.equal(vout_p[b, :, :n], vref[0][b, :, :n]) and torch.equal(vlse[b, :, :n], vref[1][b, :, :n])
+    assert torch.equal(vratio, vref[3]) and torch.equal(kvout, kvref[0]) and torch.equal(kvlse, kvref[1])
