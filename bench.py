@@ -209,38 +209,42 @@ def main() -> int:
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
-    # Two variants compared under the same clock: blocks of launches of each,
-    # alternated in A B B A order over several rounds, so that a clock that
-    # drifts during the measurement weighs on both alike.
-    def paired(fa, fb, reps, rounds=6):
+    # Two variants compared under the same clock: launches alternate between
+    # them (A B B A ...), each timed by its own events, and the comparison is
+    # the median over neighbouring pairs, so that a clock that drifts or dips
+    # during the measurement weighs on both alike.
+    def paired(fa, fb, reps):
         for _ in range(Wm):
             fa()
             fb()
         torch.cuda.synchronize()
-        per = max(1, reps // rounds)
-        tot = [0.0, 0.0]
-        for r in range(rounds):
+        ev = []
+        for r in range(reps):
+            pair = {}
             for which in ((0, 1) if r % 2 == 0 else (1, 0)):
-                fn = fa if which == 0 else fb
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
                 a.record(stream)
-                for _ in range(per):
-                    fn()
+                (fa if which == 0 else fb)()
                 b.record(stream)
-                torch.cuda.synchronize()
-                tot[which] += a.elapsed_time(b)
-        return tot[0] / (per * rounds), tot[1] / (per * rounds)
+                pair[which] = (a, b)
+            ev.append(pair)
+        torch.cuda.synchronize()
+        ta = [p[0][0].elapsed_time(p[0][1]) for p in ev]
+        tb = [p[1][0].elapsed_time(p[1][1]) for p in ev]
+        rel = sorted((y - x) / x for x, y in zip(ta, tb))
+        med = lambda xs: sorted(xs)[len(xs) // 2]
+        return med(ta), med(tb), 100.0 * rel[len(rel) // 2]
 
     run_plain = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, 0, None, None, 0.0, stream)
     run_lazy = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, stream)
     # the same step writing the layer's streaming slice from the prefill itself
     run_emit = lambda: api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, k_st, v_st,
                                                          None, 0.0, stream)
-    plain_ms, lazy_ms = paired(run_plain, run_lazy, K)
-    log(f"plain prefill: {plain_ms:.3f} ms, with the lazy ratio: {lazy_ms:.3f} ms")
-    lazy2_ms, emit_ms = paired(run_lazy, run_emit, K)
-    log(f"prefill writing the streaming slice: {emit_ms:.3f} ms (without: {lazy2_ms:.3f} ms)")
+    plain_ms, lazy_ms, lazy_pct = paired(run_plain, run_lazy, K)
+    log(f"plain prefill: {plain_ms:.3f} ms, with the lazy ratio: {lazy_ms:.3f} ms ({lazy_pct:+.2f}%)")
+    lazy2_ms, emit_ms, emit_pct = paired(run_lazy, run_emit, K)
+    log(f"prefill writing the streaming slice: {emit_ms:.3f} ms (without: {lazy2_ms:.3f} ms, {emit_pct:+.2f}%)")
     st_ms = timed(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, stream), K)
     st_fl = streaming_flop(B, Hq, N, D, S, R)
     log(f"streaming: {st_ms:.3f} ms, {st_fl / st_ms / 1e9:.1f} TFLOP/s")
@@ -266,10 +270,11 @@ def main() -> int:
         "prefill_lazy": {"kernel_ms": round(kern_ms, 4), "tflops": round(achieved, 2),
                          "frac_mfma_peak": round(achieved * 1e12 / PEAK_BF16, 4),
                          "flop_per_launch": fl},
-        # with and without the lazy ratio, timed in alternating blocks (A B B A)
-        "lazy_overhead_pct": round(100.0 * (lazy_ms - plain_ms) / plain_ms, 3),
+        # with and without the lazy ratio, launches alternated (A B B A ...):
+        # the median over neighbouring pairs of the relative difference
+        "lazy_overhead_pct": round(lazy_pct, 3),
         "prefill_emit": {"ms": round(emit_ms, 4), "ms_without_slice": round(lazy2_ms, 4),
-                         "overhead_pct": round(100.0 * (emit_ms - lazy2_ms) / lazy2_ms, 3),
+                         "overhead_pct": round(emit_pct, 3),
                          "what": "prefill+LSE+lazy ratio also writing the 4 MiB sink+recent KV slice "
                                  "(replaces the compaction kernel)"},
         "prefill_plain": {"ms": round(plain_ms, 4),
@@ -427,8 +432,14 @@ def main() -> int:
         "hbm_read_gbps": round(rbuf.numel() / (read_ms * 1e-3) / 1e9, 1),
         "spec_mfma_bf16_tflops": PEAK_BF16 / 1e12, "spec_hbm_gbps": PEAK_HBM / 1e9,
         "probes": "lt_probe_mfma_bf16: 2048 workgroups x 4 waves, 8 independent 16x16x32 bf16 "
-                  "MFMA chains per wave on pseudo-random unit-size register operands, 20000 iterations; lt_probe_read: one pass of 16-byte nontemporal loads over 4 GiB (contiguous share per workgroup), "
-                  "8192 workgroups; best of 3"}
+                  "MFMA chains per wave on pseudo-random unit-size register operands, 20000 iterations; "
+                  "lt_probe_read: one pass of 16-byte nontemporal loads over 4 GiB (contiguous share per "
+                  "workgroup), 8192 workgroups; best of 3"}
+    mp = result["measured_peaks"]
+    # the headline kernels against what this machine delivers, next to the spec fractions
+    mp["prefill_lazy_frac_of_measured_mfma"] = round(achieved / mp["mfma_bf16_tflops"], 4)
+    if "decode" in result:
+        mp["decode_frac_of_measured_read"] = round(result["decode"]["gbps"] / mp["hbm_read_gbps"], 4)
     log(f"measured peaks: {result['measured_peaks']['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
         f"{result['measured_peaks']['hbm_read_gbps']} GB/s read")
     del rbuf, rsink, psink
