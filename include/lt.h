@@ -42,9 +42,14 @@
  *   Streams: device calls are asynchronous on the given stream, never
  *   synchronise, and write their outputs only; results are valid once the
  *   stream reaches that point.
- *   Errors: every argument is checked before anything is launched, so a
- *   non-zero status leaves every output untouched.  lt_last_error() returns
- *   the calling thread's last message.  Nothing throws or aborts.
+ *   Errors: every argument is checked before anything is launched, so any
+ *   status other than LT_ERR_HIP leaves every output untouched.  LT_ERR_HIP
+ *   means the HIP runtime refused a launch; a call that launches several
+ *   kernels (prefill with W > 0, decode) may then already have queued the
+ *   earlier ones, so its outputs can be partly written.  A stale error left
+ *   in the calling thread's HIP error state by unrelated earlier work is
+ *   cleared before the first launch and not reported.  lt_last_error()
+ *   returns the calling thread's last message.  Nothing throws or aborts.
  */
 #ifndef LT_H
 #define LT_H
@@ -116,9 +121,11 @@ int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt
 
 /*
  * Workspace for lt_hybrid_decode_attn at these sizes, in bytes: the split
- * partial states, (parts + B - 1) * Hq * (D + 2) fp32.  The same size also
- * serves lt_hybrid_decode_attn_varlen with max_kv_len = kv_len.  Host-only;
- * no device call.  Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE (D).
+ * partial states, (parts + B - 1) * Hq * (D + 2) fp32.  The number of parts
+ * is chosen per (sequence, KV head) unit, so the size depends on Hkv as well
+ * as on B, Hq, D and kv_len.  The same size also serves
+ * lt_hybrid_decode_attn_varlen with max_kv_len = kv_len.  Host-only; no
+ * device call.  Errors: LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE (D).
  */
 int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len,
                                      size_t *bytes);
@@ -253,8 +260,9 @@ int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64
  * form: after layer `layer` finishes, push (score, layer); while the queue
  * holds more than C layers, the one with the highest score leaves (equal
  * scores: the lower layer index) and becomes a streaming layer.  *evicted
- * receives that layer or -1.  Layers must be pushed in order 0..L-1.  Host
- * memory is owned by the handle.
+ * receives that layer or -1.  Layers must be pushed in order 0..L-1: a
+ * layer out of order, or a push after layer L-1, is LT_ERR_VALUE and leaves
+ * the queue unchanged.  Host memory is owned by the handle.
  */
 typedef struct lt_lazy_queue lt_lazy_queue;
 int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out);
@@ -317,25 +325,37 @@ int lt_select_offline(const float *head_ratio, int P, int L, int n, int C, doubl
                       uint8_t *is_streaming);
 
 /*
- * Measurement probes, not part of the path: the matrix-core and HBM-read
- * rates the chip delivers in practice, reported next to the published peaks
- * that roofline fractions are taken against.  Both are asynchronous on
- * `stream`; the caller times them (e.g. with events on that stream).
- *   lt_probe_mfma_bf16: `blocks` workgroups of 4 waves; each wave runs
- *     `iters` rounds of 8 independent 16x16x32 bf16 matrix-core products
- *     (16384 FLOP each), i.e. blocks*4*iters*8*16384 FLOP, on pseudo-random
- *     register operands of unit size (the sustained rate depends on the
- *     data; constant operands run faster).  sink: device fp32
- *     [blocks*256], overwritten with meaningless values.
- *   lt_probe_read: reads `bytes` of device memory at `buf` once (16-byte
- *     aligned, bytes a multiple of 16) with `blocks` workgroups of 256
- *     lanes, in nontemporal 16-byte loads.  sink: device u32 [blocks], written only on an unlikely value.
- * Errors: LT_ERR_NULL (null pointer), LT_ERR_SHAPE (blocks < 1, iters < 1,
- * bytes not a positive multiple of 16), LT_ERR_LAYOUT (buf not 16-byte
- * aligned), LT_ERR_HIP (launch failure).
+ * KV bytes the prefill holds while it walks the layers ([P1] solution 2:
+ * the queue bounds peak prefill memory at C full layers, the rest
+ * streaming).  Every layer has the same sizes: full_bytes at full size,
+ * stream_bytes once switched (lt_kv_bytes); with emit != 0 each prefill also
+ * wrote its streaming slice (lt_prefill_attn_lse_lazy_emit), so a layer still
+ * at full size holds full_bytes + stream_bytes and switching keeps the slice.
+ * At step l (after layer l's push):
+ *   transient[l]: layers 0..l-1 at their current size plus layer l at full
+ *     size, before the queue's decision -- except that with
+ *     LT_EVICT_BEFORE_PUSH an earlier layer evicted at this step is already
+ *     switched (its memory is freed for layer l);
+ *   retained[l]: every layer 0..l at its size after the decision.
+ *
+ * Online form: lt_lazy_queue_set_kv_bytes sets the sizes (before the first
+ * push); after each push lt_lazy_queue_kv_bytes returns that step's pair.
+ * Errors: LT_ERR_NULL; LT_ERR_VALUE (negative sizes, sizes not set, or no
+ * layer pushed yet).
  */
-int lt_probe_mfma_bf16(int blocks, int iters, float *sink, hipStream_t stream);
-int lt_probe_read(const void *buf, size_t bytes, int blocks, unsigned *sink, hipStream_t stream);
+int lt_lazy_queue_set_kv_bytes(lt_lazy_queue *queue, int64_t full_bytes, int64_t stream_bytes, int emit);
+int lt_lazy_queue_kv_bytes(const lt_lazy_queue *queue, int64_t *retained, int64_t *transient);
+
+/*
+ * Batch form: the same pairs for a whole run from its evicted_at_step [L]
+ * (as lt_select_lazy_layers_policy writes it, policy the same) into
+ * retained [L] and transient [L].  Host-only.  Errors: LT_ERR_NULL,
+ * LT_ERR_SHAPE (L < 1), LT_ERR_VALUE (unknown policy, negative sizes, an
+ * entry that is not -1 or a layer 0..l, or a layer evicted twice); outputs
+ * are untouched on error.
+ */
+int lt_kv_accounting(const int *evicted_at_step, int L, int policy, int64_t full_bytes,
+                     int64_t stream_bytes, int emit, int64_t *retained, int64_t *transient);
 
 /* Name of a status code, and the calling thread's last error message. */
 const char *lt_status_str(int status);

@@ -1,4 +1,5 @@
-"""ctypes loader for liblt.so: declares every exported symbol of include/lt.h.
+"""ctypes loader for liblt.so: declares every exported symbol of include/lt.h
+and include/lt_probe.h.
 
 The library must exist (built by ``python -m kv_cache_compression_causal_amd.build``
 or ``__graft_entry__.build()``); there is no fallback of any kind.
@@ -15,7 +16,7 @@ LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_LAYOUT, LT_ERR_WORKSPACE,
 LT_F32, LT_BF16 = 0, 1
 LT_EVICT_AFTER_PUSH, LT_EVICT_BEFORE_PUSH = 0, 1
 
-# Every symbol include/lt.h declares.
+# Every symbol include/lt.h and include/lt_probe.h declare.
 EXPORTS = (
     "lt_prefill_attn_lse_lazy", "lt_streaming_attn", "lt_hybrid_decode_workspace_bytes",
     "lt_hybrid_decode_attn", "lt_compact_kv_streaming", "lt_kv_bytes", "lt_lazy_queue_create",
@@ -24,6 +25,7 @@ EXPORTS = (
     "lt_select_lazy_layers_policy", "lt_stream_cache_append", "lt_select_offline",
     "lt_prefill_attn_lse_lazy_varlen", "lt_streaming_attn_varlen", "lt_hybrid_decode_attn_varlen",
     "lt_compact_kv_streaming_varlen", "lt_stream_cache_append_varlen", "lt_prefill_attn_lse_lazy_emit",
+    "lt_lazy_queue_set_kv_bytes", "lt_lazy_queue_kv_bytes", "lt_kv_accounting",
 )
 
 
@@ -122,6 +124,13 @@ def lib() -> ctypes.CDLL:
     L.lt_stream_cache_append_varlen.argtypes = [LtView, LtView, c_void_p, c_void_p, c_int, c_int, c_int,
                                                 c_int, c_int, c_int, c_void_p, c_void_p]
     L.lt_stream_cache_append_varlen.restype = c_int
+    L.lt_lazy_queue_set_kv_bytes.argtypes = [c_void_p, c_int64, c_int64, c_int]
+    L.lt_lazy_queue_set_kv_bytes.restype = c_int
+    L.lt_lazy_queue_kv_bytes.argtypes = [c_void_p, ctypes.POINTER(c_int64), ctypes.POINTER(c_int64)]
+    L.lt_lazy_queue_kv_bytes.restype = c_int
+    L.lt_kv_accounting.argtypes = [ctypes.POINTER(c_int), c_int, c_int, c_int64, c_int64, c_int,
+                                   ctypes.POINTER(c_int64), ctypes.POINTER(c_int64)]
+    L.lt_kv_accounting.restype = c_int
     L.lt_status_str.argtypes = [c_int]
     L.lt_status_str.restype = ctypes.c_char_p
     L.lt_last_error.argtypes = []

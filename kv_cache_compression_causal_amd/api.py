@@ -325,6 +325,16 @@ class LazyQueue:
                                               hr.size, ctypes.byref(sc), ctypes.byref(ev)))
         return ev.value, sc.value
 
+    def set_kv_bytes(self, full_bytes: int, stream_bytes: int, emit: bool = False) -> None:
+        """Per-layer KV sizes for the queue's byte accounting (before the first push)."""
+        check(lib().lt_lazy_queue_set_kv_bytes(self._h, int(full_bytes), int(stream_bytes), int(bool(emit))))
+
+    def kv_bytes(self) -> Tuple[int, int]:
+        """(retained, transient) KV bytes of the last push's step."""
+        r, t = ctypes.c_int64(), ctypes.c_int64()
+        check(lib().lt_lazy_queue_kv_bytes(self._h, ctypes.byref(r), ctypes.byref(t)))
+        return r.value, t.value
+
     def close(self) -> None:
         if self._h:
             lib().lt_lazy_queue_destroy(self._h)
@@ -354,6 +364,21 @@ def lt_select_lazy_layers(head_ratio, C: int, policy: int = 0):
         ev.ctypes.data_as(ctypes.POINTER(ctypes.c_int)),
         st.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))))
     return score, ev, st
+
+
+def lt_kv_accounting(evicted_at_step, full_bytes: int, stream_bytes: int, policy: int = 0,
+                     emit: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-step (retained [L], transient [L]) KV bytes of a run from its
+    evicted_at_step [L] (lt_kv_accounting)."""
+    ev = np.ascontiguousarray(np.asarray(evicted_at_step, dtype=np.int32).reshape(-1))
+    L = ev.size
+    ret = np.empty(L, dtype=np.int64)
+    tra = np.empty(L, dtype=np.int64)
+    check(lib().lt_kv_accounting(ev.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), L, int(policy),
+                                 int(full_bytes), int(stream_bytes), int(bool(emit)),
+                                 ret.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                 tra.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+    return ret, tra
 
 
 def lt_select_offline(head_ratio, C: int):

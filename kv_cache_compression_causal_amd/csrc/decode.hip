@@ -530,8 +530,10 @@ size_t decode_ws_bytes(int B, int Hq, int D, int n_parts) {
 }
 
 namespace {
+// The split kernel, then the merge; each launch is checked, so a refused
+// merge launch is reported even though the split kernel is already queued.
 template <int D>
-void launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
+hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
     const bool uni = a.kv_lens == nullptr;
     if (dtype == LT_BF16) {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv))
@@ -540,6 +542,8 @@ void launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
             hipLaunchKernelGGL((decode_bf16_kernel<D, true>), grid, dim3(256), 0, st, a);
         else
             hipLaunchKernelGGL((decode_bf16_kernel<D, false>), grid, dim3(256), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((decode_combine_kernel<D, bf16>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     } else {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hq))
@@ -548,17 +552,16 @@ void launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
             hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
         else
             hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(64), 0, st, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
         hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     }
+    return hipGetLastError();
 }
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
-    if (a.D == 64)
-        launch_decode_d<64>(a, dtype, st);
-    else
-        launch_decode_d<128>(a, dtype, st);
-    return hipGetLastError();
+    return a.D == 64 ? launch_decode_d<64>(a, dtype, st) : launch_decode_d<128>(a, dtype, st);
 }
 
 }  // namespace lt

@@ -36,11 +36,36 @@ inline bool above(const Entry &a, const Entry &b) {
     return a.score > b.score || (a.score == b.score && a.layer < b.layer);
 }
 
+// KV bytes held while the prefill walks the layers (every layer the same
+// sizes): n_switched layers are at their streaming size, the rest of the
+// layers pushed so far at full size (plus their slice when the prefill wrote
+// it).  step() gives one step's pair from the decision it made.
+struct KvTally {
+    int64_t full = 0, stream = 0;
+    bool emit = false;
+    int n_switched = 0;
+    int64_t retained = 0, transient = 0;
+
+    int64_t at_full() const { return emit ? full + stream : full; }
+    // Layer `layer` was pushed under `policy` and `evicted` left (or -1).
+    void step(int layer, int evicted, int policy) {
+        // With eviction before the push, an earlier layer leaving at this
+        // step frees its memory before the current layer's KV is counted.
+        const int freed_first = policy == LT_EVICT_BEFORE_PUSH && evicted >= 0 && evicted < layer;
+        const int64_t sw = n_switched + freed_first;
+        transient = (layer - sw) * at_full() + sw * stream + at_full();
+        if (evicted >= 0) n_switched++;
+        retained = (int64_t)(layer + 1 - n_switched) * at_full() + (int64_t)n_switched * stream;
+    }
+};
+
 }  // namespace
 
 struct lt_lazy_queue {
     int L, C, next, policy;
     std::vector<Entry> heap;  // binary max-heap under above()
+    bool kv_set = false;
+    KvTally kv;
 
     // One step: layer e.layer arrives; returns the layer evicted, or -1.
     int step(const Entry &e) {
@@ -120,10 +145,60 @@ int lt_lazy_queue_create(int L, int C, lt_lazy_queue **out) {
 
 int lt_lazy_queue_push(lt_lazy_queue *q, int layer, double score, int *evicted) {
     if (q == nullptr || evicted == nullptr) return qfail(LT_ERR_NULL, "queue/evicted is NULL");
+    if (q->next >= q->L) return qfail(LT_ERR_VALUE, "all L layers have been pushed");
     if (layer != q->next) return qfail(LT_ERR_VALUE, "layers must be pushed in order");
     if (isnan(score) || isinf(score)) return qfail(LT_ERR_VALUE, "score must be finite");
     *evicted = q->step(Entry{score, layer});
+    if (q->kv_set) q->kv.step(layer, *evicted, q->policy);
     q->next++;
+    return qfail(LT_OK, "");
+}
+
+int lt_lazy_queue_set_kv_bytes(lt_lazy_queue *q, int64_t full_bytes, int64_t stream_bytes, int emit) {
+    if (q == nullptr) return qfail(LT_ERR_NULL, "queue is NULL");
+    if (full_bytes < 0 || stream_bytes < 0) return qfail(LT_ERR_VALUE, "sizes must be >= 0");
+    if (q->next != 0) return qfail(LT_ERR_VALUE, "set the KV sizes before the first push");
+    q->kv = KvTally{};
+    q->kv.full = full_bytes;
+    q->kv.stream = stream_bytes;
+    q->kv.emit = emit != 0;
+    q->kv_set = true;
+    return qfail(LT_OK, "");
+}
+
+int lt_lazy_queue_kv_bytes(const lt_lazy_queue *q, int64_t *retained, int64_t *transient) {
+    if (q == nullptr || retained == nullptr || transient == nullptr)
+        return qfail(LT_ERR_NULL, "queue/retained/transient is NULL");
+    if (!q->kv_set) return qfail(LT_ERR_VALUE, "KV sizes not set");
+    if (q->next == 0) return qfail(LT_ERR_VALUE, "no layer pushed yet");
+    *retained = q->kv.retained;
+    *transient = q->kv.transient;
+    return qfail(LT_OK, "");
+}
+
+int lt_kv_accounting(const int *evicted_at_step, int L, int policy, int64_t full_bytes, int64_t stream_bytes,
+                     int emit, int64_t *retained, int64_t *transient) {
+    if (evicted_at_step == nullptr || retained == nullptr || transient == nullptr)
+        return qfail(LT_ERR_NULL, "NULL argument");
+    if (L < 1) return qfail(LT_ERR_SHAPE, "L must be >= 1");
+    if (policy != LT_EVICT_AFTER_PUSH && policy != LT_EVICT_BEFORE_PUSH)
+        return qfail(LT_ERR_VALUE, "unknown eviction policy");
+    if (full_bytes < 0 || stream_bytes < 0) return qfail(LT_ERR_VALUE, "sizes must be >= 0");
+    std::vector<uint8_t> gone((size_t)L, 0);
+    for (int l = 0; l < L; ++l) {
+        const int e = evicted_at_step[l];
+        if (e < -1 || e > l) return qfail(LT_ERR_VALUE, "evicted_at_step[l] must be -1 or a layer 0..l");
+        if (e >= 0 && gone[e]++) return qfail(LT_ERR_VALUE, "a layer is evicted twice");
+    }
+    KvTally t;
+    t.full = full_bytes;
+    t.stream = stream_bytes;
+    t.emit = emit != 0;
+    for (int l = 0; l < L; ++l) {
+        t.step(l, evicted_at_step[l], policy);
+        retained[l] = t.retained;
+        transient[l] = t.transient;
+    }
     return qfail(LT_OK, "");
 }
 

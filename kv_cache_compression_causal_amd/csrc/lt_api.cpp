@@ -1,5 +1,6 @@
 // C-ABI shim: argument validation, launch configuration and status codes.
-// Every check runs before the first launch, so a failing call writes nothing.
+// Every check runs before the first launch, so a failing call writes nothing
+// unless the runtime refuses a launch after an earlier one of the same call.
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -7,6 +8,7 @@
 
 #include "lt.h"
 #include "lt_internal.h"
+#include "lt_probe.h"
 
 namespace {
 
@@ -29,6 +31,12 @@ int hip_status(hipError_t e, const char *what) {
     if (e != hipSuccess) return fail(LT_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
     return ok();
 }
+
+// The launchers report a launch's status through hipGetLastError, which also
+// returns (and clears) an error left in this thread's HIP state by earlier,
+// unrelated work.  Called once validation has passed, right before a call's
+// first launch, so that only this call's launches are reported.
+void clear_stale_error() { (void)hipGetLastError(); }
 
 int elem_size(int dtype) { return dtype == LT_BF16 ? 2 : dtype == LT_F32 ? 4 : 0; }
 
@@ -115,6 +123,7 @@ int prefill(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, lt
     if (k_st != nullptr)
         a.st = lt::StreamOut{k_st->data, v_st->data, k_st->sb, k_st->sh, k_st->sn, v_st->sb, v_st->sh, v_st->sn};
     const int mode = W > 0 ? lt::MODE_FULL_LAZY : lt::MODE_FULL;
+    clear_stale_error();
     hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, mode, stream)
                                             : lt::launch_attn_f32(a, shape->D, mode, stream);
     if (he != hipSuccess) return hip_status(he, "prefill launch");
@@ -137,6 +146,7 @@ int streaming(const lt_shape *shape, const int32_t *lens, lt_view q, lt_view k, 
         return fail(LT_ERR_SHAPE, "need S >= 0, R >= 1, S + R <= 2^30 (got S=%d, R=%d)", S, R);
     lt::AttnArgs a = make_args(shape, q, k, v, out, lse, S, R, 0, nullptr);
     a.seq_len = lens;
+    clear_stale_error();
     hipError_t he = shape->dtype == LT_BF16 ? lt::launch_attn_bf16(a, shape->D, lt::MODE_STREAM, stream)
                                             : lt::launch_attn_f32(a, shape->D, lt::MODE_STREAM, stream);
     if (he != hipSuccess) return hip_status(he, "streaming launch");
@@ -188,6 +198,7 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     }
     a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
     a.c = a.scale * 1.4426950408889634f;
+    clear_stale_error();
     return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
 }
 
@@ -210,6 +221,7 @@ int compact(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, 
     a.B = B; a.Hkv = Hkv; a.N = N; a.D = D; a.elem = elem_size(dtype); a.S = S; a.R = R;
     a.rows_out = N <= S + R ? N : S + R;
     a.seq_len = lens;
+    clear_stale_error();
     return hip_status(lt::launch_compact(a, stream), "compaction launch");
 }
 
@@ -231,6 +243,7 @@ int append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_
     a.B = B; a.Hkv = Hkv; a.D = D; a.elem = elem_size(dtype);
     a.slot = pos < S ? pos : S + (pos - S) % R;
     a.S = S; a.R = R; a.pos = pos_dev;
+    clear_stale_error();
     return hip_status(lt::launch_append(a, stream), "append launch");
 }
 
@@ -353,6 +366,7 @@ int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64
 int lt_probe_mfma_bf16(int blocks, int iters, float *sink, hipStream_t stream) {
     if (sink == nullptr) return fail(LT_ERR_NULL, "sink is NULL");
     if (blocks < 1 || iters < 1) return fail(LT_ERR_SHAPE, "blocks and iters must be >= 1");
+    clear_stale_error();
     return hip_status(lt::launch_mfma_probe(blocks, iters, sink, stream), "mfma probe launch");
 }
 
@@ -360,6 +374,7 @@ int lt_probe_read(const void *buf, size_t bytes, int blocks, unsigned *sink, hip
     if (buf == nullptr || sink == nullptr) return fail(LT_ERR_NULL, "buf/sink is NULL");
     if (blocks < 1 || bytes == 0 || bytes % 16) return fail(LT_ERR_SHAPE, "bad probe sizes");
     if (!aligned16(buf)) return fail(LT_ERR_LAYOUT, "buf not 16-byte aligned");
+    clear_stale_error();
     return hip_status(lt::launch_read_probe(buf, bytes, blocks, sink, stream), "read probe launch");
 }
 

@@ -9,8 +9,9 @@ Chinese write-up, "solution 2"):
      the sink + recent rows and the full copy released (or, with eviction
      before the push, the highest of the C already queued leaves first).
 The KV bytes held after each step (and while a layer's full KV is added,
-before the queue's decision) are tracked, so the peak prefill KV can be
-checked against C full layers + the rest streaming.
+before the queue's decision) are tracked by the library's queue
+(lt_lazy_queue_kv_bytes), so the peak prefill KV can be checked against C
+full layers + the rest streaming.
 
 Run the 64-layer workload:  python -m kv_cache_compression_causal_amd.driver
 Offline selection over P prompts:  python -m kv_cache_compression_causal_amd.driver --offline P
@@ -77,8 +78,10 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
             lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
             rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
             ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+        if l == 0:
             dt = LT_BF16 if q.dtype == torch.bfloat16 else LT_F32
             full_b, stream_b = api.lt_kv_bytes(B, Hkv, N, D, dt, S, R)
+            queue.set_kv_bytes(full_b, stream_b, emit)
         if timing:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -99,11 +102,9 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
         kv[l] = (k, v)
         del q
         ev, score = queue.push_ratios(l, r)
-        freed_first = policy == LT_EVICT_BEFORE_PUSH and 0 <= ev < l
-        at_full = full_b + stream_b if emit else full_b
-        held = sum(stream_b if (is_stream[x] or (freed_first and x == ev)) else at_full
-                   for x in range(l)) + at_full
-        transient.append(held)
+        held_after, held_before = queue.kv_bytes()
+        transient.append(held_before)
+        retained.append(held_after)
         if ev >= 0:
             kf, vf = kv.pop(ev)
             if emit:
@@ -115,8 +116,6 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
         head_ratio.append([float(x) for x in r])
         scores.append(score)
         evicted.append(ev)
-        retained.append(sum(stream_b if is_stream[x] else (full_b + stream_b if emit else full_b)
-                            for x in range(l + 1)))
     torch.cuda.synchronize()
     queue.close()
     return DriverResult(layers, capacity, head_ratio, scores, evicted, is_stream, retained, transient,

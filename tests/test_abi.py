@@ -19,7 +19,8 @@ import oracle
 from kv_cache_compression_causal_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "lt.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -31,9 +32,11 @@ def L():
 
 
 def header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return set(re.findall(r"\b(lt_[a-z0-9_]+)\s*\(", text))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(lt_[a-z0-9_]+)\s*\(", text))
+    return names
 
 
 def test_exports_every_declared_function(L):
@@ -201,6 +204,101 @@ def test_queue_errors(L):
     assert e.value.status == _lib.LT_ERR_VALUE
     with pytest.raises(_lib.LtError):
         api.lt_select_lazy_layers(np.zeros((3, 2), dtype=np.float32), 1, 2)
+
+
+def test_queue_rejects_push_past_last_layer(L):
+    """A queue of L layers accepts exactly the pushes 0..L-1; one more is
+    LT_ERR_VALUE and leaves the queue as it was (no entry added)."""
+    from kv_cache_compression_causal_amd import api
+    q = api.LazyQueue(3, 1)
+    evs = [q.push(l, s) for l, s in enumerate((0.5, 0.2, 0.9))]
+    assert evs == oracle.select_lazy_layers([0.5, 0.2, 0.9], 1)[0]
+    ev = ctypes.c_int(-7)
+    assert L.lt_lazy_queue_push(q._h, 3, 0.1, ctypes.byref(ev)) == _lib.LT_ERR_VALUE
+    assert ev.value == -7
+    assert b"pushed" in L.lt_last_error()
+    r = (ctypes.c_float * 2)(0.1, 0.2)
+    assert L.lt_lazy_queue_push_ratios(q._h, 3, r, 2, None, ctypes.byref(ev)) == _lib.LT_ERR_VALUE
+    q.close()
+
+
+def _random_run(rnd):
+    Lyr = rnd.randint(1, 40)
+    C = rnd.randint(0, Lyr)
+    scores = [rnd.choice([rnd.random(), 0.5, 0.25]) for _ in range(Lyr)]
+    return Lyr, C, scores
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_kv_accounting_matches_oracle(L, seed):
+    """The library's per-step KV bytes (batch call, and the online queue's
+    counters after each push) equal the oracle's accounting for the same
+    decisions, under both eviction timings, with and without slices written
+    by the prefill."""
+    from kv_cache_compression_causal_amd import api
+    rnd = random.Random(7000 + seed)
+    Lyr, C, scores = _random_run(rnd)
+    full, stream = rnd.choice([(134217728, 4194304), (1000, 300), (8, 8), (0, 0)])
+    for policy, pname in ((_lib.LT_EVICT_AFTER_PUSH, "after"), (_lib.LT_EVICT_BEFORE_PUSH, "before")):
+        ev, _ = oracle.select_lazy_layers(scores, C, policy=pname)
+        for emit in (False, True):
+            want = oracle.kv_accounting(ev, full, stream, policy=pname, emit=emit)
+            ret, tra = api.lt_kv_accounting(ev, full, stream, policy, emit)
+            assert list(ret) == want["retained"] and list(tra) == want["transient"]
+            q = api.LazyQueue(Lyr, C, policy)
+            q.set_kv_bytes(full, stream, emit)
+            got_r, got_t = [], []
+            for l, sc in enumerate(scores):
+                assert q.push(l, sc) == ev[l]
+                r, t = q.kv_bytes()
+                got_r.append(r)
+                got_t.append(t)
+            q.close()
+            assert got_r == want["retained"] and got_t == want["transient"]
+
+
+def test_kv_accounting_driver64_closed_form(L):
+    """64 layers of 128 MiB full / 4 MiB streaming KV, capacity 32, layer
+    scores rising with the layer index (each push evicts the new layer once
+    the queue is full): all-full 8192 MiB, final 4224 MiB, peak 4348 MiB (33
+    full + 31 streaming while layer 63 is added)."""
+    from kv_cache_compression_causal_amd import api
+    MiB = 1 << 20
+    ev, _ = oracle.select_lazy_layers([l / 64 for l in range(64)], 32)
+    ret, tra = api.lt_kv_accounting(ev, 128 * MiB, 4 * MiB)
+    assert ret[-1] == 4224 * MiB and max(tra) == 4348 * MiB and tra[-1] == 4348 * MiB
+
+
+def test_kv_accounting_errors(L):
+    from kv_cache_compression_causal_amd import api
+    i64 = ctypes.POINTER(ctypes.c_int64)
+    ret = np.full(3, -5, dtype=np.int64)
+    tra = np.full(3, -5, dtype=np.int64)
+    f = L.lt_kv_accounting
+
+    def call(ev, policy=0, full=10, stream=2, n=None):
+        e = np.asarray(ev, dtype=np.int32)
+        return f(e.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), len(ev) if n is None else n, policy, full, stream,
+                 0, ret.ctypes.data_as(i64), tra.ctypes.data_as(i64))
+
+    assert call([-1, 3, -1]) == _lib.LT_ERR_VALUE     # evicts a future layer
+    assert call([-1, 0, 0]) == _lib.LT_ERR_VALUE      # evicts layer 0 twice
+    assert call([-2, -1, -1]) == _lib.LT_ERR_VALUE
+    assert call([-1, -1, -1], policy=5) == _lib.LT_ERR_VALUE
+    assert call([-1, -1, -1], full=-1) == _lib.LT_ERR_VALUE
+    assert call([-1, -1, -1], n=0) == _lib.LT_ERR_SHAPE
+    assert list(ret) == [-5] * 3 and list(tra) == [-5] * 3   # untouched on error
+    assert f(None, 3, 0, 10, 2, 0, ret.ctypes.data_as(i64), tra.ctypes.data_as(i64)) == _lib.LT_ERR_NULL
+    q = api.LazyQueue(3, 1)
+    r, t = ctypes.c_int64(), ctypes.c_int64()
+    assert L.lt_lazy_queue_kv_bytes(q._h, ctypes.byref(r), ctypes.byref(t)) == _lib.LT_ERR_VALUE  # not set
+    q.set_kv_bytes(10, 2)
+    assert L.lt_lazy_queue_kv_bytes(q._h, ctypes.byref(r), ctypes.byref(t)) == _lib.LT_ERR_VALUE  # no push
+    q.push(0, 0.5)
+    with pytest.raises(_lib.LtError):
+        q.set_kv_bytes(10, 2)   # after the first push
+    assert L.lt_lazy_queue_set_kv_bytes(None, 1, 1, 0) == _lib.LT_ERR_NULL
+    q.close()
 
 
 @pytest.mark.parametrize("seed", range(40))
