@@ -145,6 +145,28 @@ int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lt_hybrid_decode_attn without a workspace argument, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  Same arguments, outputs,
+ * kernels and results as lt_hybrid_decode_attn (bit for bit); the split
+ * partial states go to a fixed scratch array the library holds on each GPU
+ * (LT_DECODE_NOALLOC_SCRATCH_BYTES, kept until the process ends).  Sizes
+ * whose workspace (lt_hybrid_decode_workspace_bytes) exceeds that are
+ * LT_ERR_WORKSPACE, checked before anything else touches the GPU.  Runs on
+ * the current device (the stream must belong to it); the first call on a
+ * device looks up that device's array (LT_ERR_HIP if that fails).  Nothing
+ * is allocated and no memory is cleared (every partial state is written
+ * before it is read).  Every call on one GPU shares that GPU's array: calls
+ * that may overlap in time there (on different streams, or from different
+ * threads without ordering) race and can give wrong results; calls on one
+ * stream run one after the other and are safe.
+ */
+#define LT_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+int lt_hybrid_decode_attn_noalloc(int B, int Hq, int Hkv, int D, int dtype, float scale,
+                                  const void *q, lt_view k_cache, lt_view v_cache, int64_t kv_len,
+                                  void *out, float *lse, hipStream_t stream);
+
+/*
  * Switch a layer's KV to the streaming version ([P1] solution 2; [P4]
  * Figure 2): copy the rows of positions [0,S) and [N-R,N) of every (b, kv
  * head) of k_full / v_full [B,Hkv,N,D] into k_stream / v_stream

@@ -26,7 +26,9 @@ EXPORTS = (
     "lt_prefill_attn_lse_lazy_varlen", "lt_streaming_attn_varlen", "lt_hybrid_decode_attn_varlen",
     "lt_compact_kv_streaming_varlen", "lt_stream_cache_append_varlen", "lt_prefill_attn_lse_lazy_emit",
     "lt_lazy_queue_set_kv_bytes", "lt_lazy_queue_kv_bytes", "lt_kv_accounting",
+    "lt_hybrid_decode_attn_noalloc",
 )
+LT_DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class LtView(ctypes.Structure):
@@ -73,6 +75,9 @@ def lib() -> ctypes.CDLL:
                                         LtView, LtView, c_int64, c_void_p, c_void_p, c_void_p,
                                         c_size_t, c_void_p]
     L.lt_hybrid_decode_attn.restype = c_int
+    L.lt_hybrid_decode_attn_noalloc.argtypes = [c_int, c_int, c_int, c_int, c_int, ctypes.c_float, c_void_p,
+                                                LtView, LtView, c_int64, c_void_p, c_void_p, c_void_p]
+    L.lt_hybrid_decode_attn_noalloc.restype = c_int
     L.lt_compact_kv_streaming.argtypes = [LtView, LtView, LtView, LtView, c_int, c_int, c_int,
                                           c_int, c_int, c_int, c_int, c_void_p]
     L.lt_compact_kv_streaming.restype = c_int

@@ -28,6 +28,7 @@
 //   rows through ds_read_b64_tr_b16.  Each wave streams its own 32-key steps
 //   with coalesced 128-bit loads, one step ahead.
 // fp32 path (vector ALUs): lane = pair of head dims, one key at a time.
+#include <mutex>
 #include <type_traits>
 
 #include "lt_internal.h"
@@ -559,6 +560,33 @@ hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
     return hipGetLastError();
 }
 }  // namespace
+
+// Workspace of lt_hybrid_decode_attn_noalloc: the split partial states in a
+// device array of fixed size, one copy per GPU, held until the process ends.
+// Host code never passes `scratch` itself to a kernel (on the host the name
+// stands for a host-side shadow, not a device address): the device address
+// is looked up once per GPU and kept.
+static __device__ __align__(256) char scratch[LT_DECODE_NOALLOC_SCRATCH_BYTES];
+
+hipError_t decode_scratch(void **ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st) {
     return a.D == 64 ? launch_decode_d<64>(a, dtype, st) : launch_decode_d<128>(a, dtype, st);

@@ -162,9 +162,11 @@ size_t decode_ws_need(int B, int Hq, int Hkv, int D, int64_t kv_len) {
     return uni > var ? uni : var;
 }
 
+// ws == nullptr with noalloc: the partial states go to the library's fixed
+// per-GPU scratch array instead of a caller's workspace.
 int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q, lt_view k_cache,
            lt_view v_cache, int64_t kv_len, const int32_t *kv_lens, void *out, float *lse, void *ws,
-           size_t ws_bytes, hipStream_t stream) {
+           size_t ws_bytes, hipStream_t stream, bool noalloc = false) {
     if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
@@ -177,6 +179,14 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     int e;
     if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
     const size_t need = decode_ws_need(B, Hq, Hkv, D, kv_len);
+    if (noalloc) {
+        if (need > LT_DECODE_NOALLOC_SCRATCH_BYTES)
+            return fail(LT_ERR_WORKSPACE, "these sizes need %zu bytes of scratch, more than the %zu the library holds",
+                        need, (size_t)LT_DECODE_NOALLOC_SCRATCH_BYTES);
+        const hipError_t he = lt::decode_scratch(&ws);
+        if (he != hipSuccess) return hip_status(he, "decode scratch lookup");
+        ws_bytes = LT_DECODE_NOALLOC_SCRATCH_BYTES;
+    }
     if (ws == nullptr) return fail(LT_ERR_NULL, "workspace is NULL");
     if (!aligned16(ws)) return fail(LT_ERR_LAYOUT, "workspace not 16-byte aligned");
     if (ws_bytes < need) return fail(LT_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
@@ -316,6 +326,13 @@ int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale,
                           void *ws, size_t ws_bytes, hipStream_t stream) {
     return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, ws, ws_bytes,
                   stream);
+}
+
+int lt_hybrid_decode_attn_noalloc(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
+                                  lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
+                                  hipStream_t stream) {
+    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, nullptr, 0, stream,
+                  true);
 }
 
 int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,

@@ -155,6 +155,9 @@ int64_t decode_split_keys(int64_t kv_len, int splits);
 int decode_num_parts(int B, int Hkv, int64_t kv_len);
 size_t decode_ws_bytes(int B, int Hq, int D, int n_parts);
 hipError_t launch_decode(const DecodeArgs &a, int dtype, hipStream_t st);
+// Device address of the current GPU's fixed decode scratch array
+// (LT_DECODE_NOALLOC_SCRATCH_BYTES), looked up on the first call per GPU.
+hipError_t decode_scratch(void **ptr);
 
 struct CompactArgs {
     const void *kf, *vf;

@@ -378,6 +378,23 @@ def test_varlen_errors(L):
     assert a(view(), view(), GOOD + 8, GOOD, 2, 2, 128, _lib.LT_BF16, 4, 60, GOOD, None) == _lib.LT_ERR_LAYOUT
 
 
+def test_noalloc_decode_validates_before_touching_the_gpu(L):
+    """lt_hybrid_decode_attn_noalloc checks its arguments, and that the
+    partial states fit the library's scratch array, before anything touches
+    the GPU (no GPU here: a lookup or launch would return LT_ERR_HIP)."""
+    f = L.lt_hybrid_decode_attn_noalloc
+    bf = _lib.LT_BF16
+    n = ctypes.c_size_t()
+    assert L.lt_hybrid_decode_workspace_bytes(1024, 16, 1, 128, 64, ctypes.byref(n)) == 0
+    assert n.value > _lib.LT_DECODE_NOALLOC_SCRATCH_BYTES
+    assert f(1024, 16, 1, 128, bf, 0.0, GOOD, view(), view(), 64, GOOD, None, None) == _lib.LT_ERR_WORKSPACE
+    assert b"scratch" in L.lt_last_error()
+    assert f(8, 40, 8, 96, bf, 0.0, GOOD, view(), view(), 1000, GOOD, None, None) == _lib.LT_ERR_DTYPE
+    assert f(8, 40, 8, 128, bf, 0.0, GOOD, view(), view(), 0, GOOD, None, None) == _lib.LT_ERR_SHAPE
+    assert f(8, 40, 8, 128, bf, 0.0, None, view(), view(), 1000, GOOD, None, None) == _lib.LT_ERR_NULL
+    assert f(8, 40, 8, 128, bf, 0.0, GOOD, view(sn=100), view(), 1000, GOOD, None, None) == _lib.LT_ERR_LAYOUT
+
+
 def test_kv_bytes_matches_oracle(L):
     from kv_cache_compression_causal_amd import api
     for (B, Hkv, N, D, dt, S, R) in [(1, 8, 32768, 128, 1, 4, 1020), (8, 8, 100000, 128, 1, 4, 1020),
