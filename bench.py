@@ -1,35 +1,49 @@
 """Benchmark of the LightTransfer-Test hot path on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-driver] [--no-cpu] [--no-varlen]
+python bench.py [--gpus 1] [--steps K] [--warmup W]
+                [--config {all,tiny,mistral8k,qwen32k,driver64,decode100k}]
+                [--S S] [--R R] [--wobs W_obs] [--seed SEED]
+                [--no-decode] [--no-driver] [--no-cpu] [--no-varlen]
 
-Headline leg (the step): one LightTransfer-Test layer at the qwen32k shape
-(B1 N32768 Hq40 Hkv8 D128 bf16, keys of tokens 0..3 x3, S4 R1020 W128):
-causal GQA prefill with LSE and the lazy-ratio epilogue + per-head mean,
-ratios to the host, layer score into the lazy-layer queue, and the KV of the
-evicted layer compacted to its sink + recent slice.  value = algorithmic
-prefill + lazy-numerator FLOP per step / wall time per step.
+Default (--config all): one JSON line whose headline is the qwen32k layer
+(B1 N32768 Hq40 Hkv8 D128 bf16, keys of tokens 0..3 x3, S4 R1020 W128),
+timed as a step of the method -- causal GQA prefill with LSE and the lazy
+ratio + per-head mean, ratios to the host, layer score and queue push in the
+library, and the KV of the evicted layer compacted to its sink + recent
+slice; value = algorithmic prefill + lazy-numerator FLOP per step / wall
+time per step.  Beside it, each workload of the pages' shapes:
+  tiny        fp32 B1 N512 Hq4 Hkv1 D64, S4 R60 W32: launch latency (median
+              of 100 launches, each timed by its own events) and the full
+              oracle's time
+  mistral8k   bf16 B1 N8192 Hq32 Hkv8 D128, S4 R1020 W64: prefill + lazy ratio,
+              the plain prefill (the ratio's overhead, launches alternated)
+              and streaming attention on the same tensors (medians of 20)
+  qwen32k     the same three numbers at the headline shape, plus the prefill
+              writing the layer's streaming slice, and a batch of four prompts
+              (32K/24K/16K/8K tokens padded to 32K)
+  decode100k  one hybrid decode step: B8, 100000-token context, 64 layers (32
+              full, 32 streaming at S+R rows), one buffer per layer, the 64
+              calls captured in a HIP graph; median of 20 replays; also with
+              eight contexts from 100000 down to 12500 tokens
+  driver64    the 64-layer LightTransfer-Test prefill with every layer's
+              inputs resident in HBM: one timed pass (prefill, per-layer
+              device->host sync, queue, compaction), the selection and the KV
+              bytes; both eviction timings, slices written by the prefill,
+              and offline selection over four prompts
+--config X measures workload X alone and makes it the headline.  --S, --R,
+--wobs and --seed replace those parameters in every workload measured.
 
-Other legs, reported beside it: the same prefill without the lazy ratio
-(its overhead), streaming attention on the same tensors, one hybrid decode
-step at B8 / 100000-token context over 64 layers (32 full, 32 streaming at
-1024 rows; one distinct buffer per layer; the 64 calls are captured once in
-a HIP graph and replayed), the 64-layer LightTransfer-Test prefill
-(selected layers, eviction order, KV bytes) and offline selection over four
-prompts, and variable-length batches: prefill over prompts of 32K/24K/16K/8K
-tokens padded to 32K, and the decode step with eight contexts from 100000
-down to 12500 tokens (lengths read per sequence on the device).
-
-roofline: the prefill+lazy kernel, FLOP per launch over its mean duration
-from HIP events on the launch stream, against the 2.5 PFLOP/s dense bf16
-matrix-core peak.  cpu_baseline: the fp64 oracle on a bounded row sample of
+roofline: the headline's dominant kernel, algorithmic FLOP (or bytes) per
+launch over its mean duration from HIP events on the launch stream, against
+the published peak.  cpu_baseline: the fp64 oracle on a bounded sample of
 the same workload, on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
-import math
 import os
 import re
 import sys
@@ -40,6 +54,9 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16 = 2.5e15      # MI355X dense bf16 matrix-core peak, FLOP/s
 PEAK_HBM = 8.0e12       # MI355X HBM3E peak, B/s
+PEAK_F32_VALU = 157.3e12  # MI355X fp32 vector peak, FLOP/s
+METRIC = "prefill attn+lazy-ratio TFLOP/s @32K (% MFMA peak); hybrid decode HBM GB/s"
+CONFIGS = ("all", "tiny", "mistral8k", "qwen32k", "driver64", "decode100k")
 
 
 def log(msg: str) -> None:
@@ -61,6 +78,12 @@ def streaming_flop(B, Hq, N, D, S, R):
     return 4.0 * B * Hq * D * tot
 
 
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
 def traffic_from_profile(src_path: str, prof_path: str):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
     if the summary is missing or the kernel source changed since."""
@@ -75,17 +98,581 @@ def traffic_from_profile(src_path: str, prof_path: str):
     return float(m_b.group(1))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class Bench:
+    """The legs of the benchmark; each returns a dict for the JSON line."""
+
+    def __init__(self, args, torch, dev):
+        self.args = args
+        self.torch = torch
+        self.dev = dev
+        self.K = args.steps
+        self.Wm = args.warmup
+        self.stream = torch.cuda.current_stream()
+        from kv_cache_compression_causal_amd import _lib, api, ops, synth
+        self._lib, self.api, self.ops, self.synth = _lib, api, ops, synth
+
+    # -- workloads with the command line's overrides ----------------------
+    def workload(self, w):
+        a = self.args
+        kw = {}
+        if a.S is not None:
+            kw["S"] = a.S
+        if a.R is not None:
+            kw["R"] = a.R
+        if a.wobs is not None and w.W > 0:
+            kw["W"] = min(a.wobs, w.N)
+        if a.seed is not None:
+            kw["seed"] = a.seed
+        return dataclasses.replace(w, **kw) if kw else w
+
+    # -- timing -----------------------------------------------------------
+    def events(self):
+        E = self.torch.cuda.Event
+        return E(enable_timing=True), E(enable_timing=True)
+
+    def time_each(self, fn, reps, warm=None):
+        """Durations (ms) of `reps` launches of fn, each bracketed by its own
+        events on the launch stream, after `warm` untimed ones."""
+        for _ in range(self.Wm if warm is None else warm):
+            fn()
+        self.torch.cuda.synchronize()
+        ev = []
+        for _ in range(reps):
+            a, b = self.events()
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            ev.append((a, b))
+        self.torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in ev]
+
+    def paired(self, fa, fb, reps):
+        """Two variants under the same clock: launches alternate (A B B A ...),
+        each timed by its own events; returns the medians of A and B and the
+        median over neighbouring pairs of the relative difference, so that a
+        clock that drifts or dips weighs on both alike."""
+        for _ in range(self.Wm):
+            fa()
+            fb()
+        self.torch.cuda.synchronize()
+        ev = []
+        for r in range(reps):
+            pair = {}
+            for which in ((0, 1) if r % 2 == 0 else (1, 0)):
+                a, b = self.events()
+                a.record(self.stream)
+                (fa if which == 0 else fb)()
+                b.record(self.stream)
+                pair[which] = (a, b)
+            ev.append(pair)
+        self.torch.cuda.synchronize()
+        ta = [p[0][0].elapsed_time(p[0][1]) for p in ev]
+        tb = [p[1][0].elapsed_time(p[1][1]) for p in ev]
+        rel = [(y - x) / x for x, y in zip(ta, tb)]
+        return median(ta), median(tb), 100.0 * median(rel)
+
+    # -- the method's step at one layer (headline) -------------------------
+    def step_leg(self, w, q, k, v):
+        """K timed steps of one LightTransfer-Test layer: prefill + LSE + lazy
+        ratio, ratios to the host through one of two pinned buffers, the
+        layer's score and queue push in the library, and compaction of the
+        evicted layer's KV.  A layer's push (and compaction) runs while the
+        next layer's prefill is on the GPU: that prefill does not depend on
+        the queue's decision, only the KV bookkeeping does."""
+        torch, api = self.torch, self.api
+        K, Wm, stream = self.K, self.Wm, self.stream
+        B, N, Hq, Hkv, D, S, R, W = w.B, w.N, w.Hq, w.Hkv, w.D, w.S, w.R, w.W
+        out = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, device=self.dev, dtype=torch.float32)
+        rows = torch.empty(B, Hq, W, device=self.dev, dtype=torch.float32)
+        srows = min(N, S + R)
+        k_st = torch.empty(B, Hkv, srows, D, device=self.dev, dtype=q.dtype)
+        v_st = torch.empty_like(k_st)
+        total_layers = K + Wm
+        queue = api.LazyQueue(total_layers, total_layers // 2)
+        ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+        layer = [0]
+        ratio_d = [torch.empty(B, Hq, device=self.dev, dtype=torch.float32) for _ in range(2)]
+        ratio_h = [torch.empty(B, Hq, dtype=torch.float32, pin_memory=True) for _ in range(2)]
+        copied = [torch.cuda.Event() for _ in range(2)]
+        pending = [None]
+
+        def finish(slot):
+            copied[slot].synchronize()  # the per-layer device->host hand-off of the method
+            evicted, _ = queue.push_ratios(layer[0], ratio_h[slot].numpy())
+            layer[0] += 1
+            if evicted >= 0:
+                # one resident layer stands in for every layer: compact it
+                api.lt_compact_kv_streaming(k, v, k_st, v_st, S, R, stream)
+
+        def step(i, timed_idx=None):
+            slot = i % 2
+            if timed_idx is not None:
+                ev0[timed_idx].record(stream)
+            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio_d[slot], 0.0, stream)
+            if timed_idx is not None:
+                ev1[timed_idx].record(stream)
+            ratio_h[slot].copy_(ratio_d[slot], non_blocking=True)
+            copied[slot].record(stream)
+            if pending[0] is not None:
+                finish(pending[0])
+            pending[0] = slot
+
+        def drain():
+            if pending[0] is not None:
+                finish(pending[0])
+                pending[0] = None
+
+        for i in range(Wm):
+            step(i)
+        drain()
+        torch.cuda.synchronize()
+        log(f"{w.name}: timing {K} steps")
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(i, i)
+        drain()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        queue.close()
+        ms_step = (t1 - t0) * 1e3 / K
+        kms = [a.elapsed_time(b) for a, b in zip(ev0, ev1)]
+        fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
+        return {"ms_per_step": ms_step, "value": fl / (ms_step * 1e-3) / 1e12, "flop": fl,
+                "kernel_ms_mean": sum(kms) / len(kms), "kernel_ms_median": median(kms)}
+
+    # -- one prefill workload: lazy ratio, its overhead, streaming ----------
+    def prefill_leg(self, w, q, k, v, emit=False):
+        torch, api = self.torch, self.api
+        B, N, Hq, Hkv, D, S, R, W = w.B, w.N, w.Hq, w.Hkv, w.D, w.S, w.R, w.W
+        out = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, device=self.dev, dtype=torch.float32)
+        rows = torch.empty(B, Hq, W, device=self.dev, dtype=torch.float32)
+        ratio = torch.empty(B, Hq, device=self.dev, dtype=torch.float32)
+        st = self.stream
+        run_plain = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, 0, None, None, 0.0, st)
+        run_lazy = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, st)
+        plain_ms, lazy_ms, lazy_pct = self.paired(run_plain, run_lazy, self.K)
+        fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
+        pfl = prefill_flop(B, Hq, N, D)
+        res = {
+            "prefill_lazy": {"ms_median": round(lazy_ms, 4), "tflops": round(fl / lazy_ms / 1e9, 2),
+                             "frac_mfma_peak": round(fl / lazy_ms / 1e9 * 1e12 / PEAK_BF16, 4),
+                             "flop_per_launch": fl},
+            "prefill_plain": {"ms_median": round(plain_ms, 4), "tflops": round(pfl / plain_ms / 1e9, 2)},
+            # launches alternated (A B B A ...): median over neighbouring pairs
+            "lazy_overhead_pct": round(lazy_pct, 3),
+        }
+        log(f"{w.name}: prefill+lazy {lazy_ms:.3f} ms ({fl / lazy_ms / 1e9:.1f} TFLOP/s), plain {plain_ms:.3f} ms "
+            f"({lazy_pct:+.2f}%)")
+        if emit:
+            srows = min(N, S + R)
+            k_st = torch.empty(B, Hkv, srows, D, device=self.dev, dtype=q.dtype)
+            v_st = torch.empty_like(k_st)
+            run_emit = lambda: api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, k_st,
+                                                                 v_st, None, 0.0, st)
+            base_ms, emit_ms, emit_pct = self.paired(run_lazy, run_emit, self.K)
+            res["prefill_emit"] = {"ms_median": round(emit_ms, 4), "ms_without_slice": round(base_ms, 4),
+                                   "overhead_pct": round(emit_pct, 3),
+                                   "what": "prefill+LSE+lazy ratio also writing the sink+recent KV slice "
+                                           "(replaces the compaction kernel)"}
+            log(f"{w.name}: writing the streaming slice {emit_pct:+.2f}%")
+            del k_st, v_st
+        sout = torch.empty_like(q)
+        slse = torch.empty_like(lse)
+        sts = self.time_each(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, st), self.K)
+        st_ms = median(sts)
+        sfl = streaming_flop(B, Hq, N, D, S, R)
+        res["streaming"] = {"ms_median": round(st_ms, 4), "ms_mean": round(sum(sts) / len(sts), 4),
+                            "tflops": round(sfl / st_ms / 1e9, 2),
+                            "frac_mfma_peak": round(sfl / st_ms / 1e9 * 1e12 / PEAK_BF16, 4), "flop": sfl}
+        log(f"{w.name}: streaming {st_ms:.3f} ms ({sfl / st_ms / 1e9:.1f} TFLOP/s)")
+        return res
+
+    # -- tiny fp32 layer ---------------------------------------------------
+    def tiny_leg(self, cpu=True):
+        torch, api = self.torch, self.api
+        w = self.workload(self.synth.TINY)
+        q, k, v = self.synth.workload_qkv(w, device=self.dev)
+        B, N, Hq, D, S, R, W = w.B, w.N, w.Hq, w.D, w.S, w.R, w.W
+        out = torch.empty_like(q)
+        lse = torch.empty(B, Hq, N, device=self.dev, dtype=torch.float32)
+        rows = torch.empty(B, Hq, W, device=self.dev, dtype=torch.float32)
+        ratio = torch.empty(B, Hq, device=self.dev, dtype=torch.float32)
+        ts = self.time_each(lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0,
+                                                                 self.stream), 100, warm=10)
+        fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
+        ms = median(ts)
+        res = {"workload": f"tiny: fp32 B{B} N{N} Hq{Hq} Hkv{w.Hkv} D{D}, S{S} R{R} W{W}, seed {w.seed}",
+               "latency_us_median": round(ms * 1e3, 2), "latency_us_min": round(min(ts) * 1e3, 2),
+               "reps": len(ts), "flop": fl, "tflops": round(fl / ms / 1e9, 4),
+               "bound": "latency (a few workgroups; parity workload, no roofline fraction)"}
+        log(f"tiny: {ms * 1e3:.1f} us per launch (median of {len(ts)})")
+        if cpu:
+            import oracle
+            qh, kh, vh = (t.double().cpu().numpy() for t in (q, k, v))
+            c0 = time.perf_counter()
+            oracle.prefill(qh, kh, vh, S=S, R=R, W=W, streaming=True)
+            t_cpu = time.perf_counter() - c0
+            res["oracle_full_ms"] = round(t_cpu * 1e3, 3)
+            res["oracle_threads"] = oracle.threads()
+            res["oracle_what"] = "full fp64 oracle: out, LSE, streaming out/LSE, lazy rows and ratios"
+        return res
+
+    # -- variable-length prefill --------------------------------------------
+    def varlen_leg(self):
+        torch, api, synth = self.torch, self.api, self.synth
+        vw, vlens = self.workload(synth.QWEN32K_VARLEN), synth.QWEN32K_VARLEN_LENS
+        log("generating the variable-length batch")
+        vq, vk, vv = synth.workload_qkv(vw, device=self.dev)
+        vout = torch.empty_like(vq)
+        vlse = torch.empty(vw.B, vw.Hq, vw.N, device=self.dev, dtype=torch.float32)
+        vrows = torch.empty(vw.B, vw.Hq, vw.W, device=self.dev, dtype=torch.float32)
+        vratio = torch.empty(vw.B, vw.Hq, device=self.dev, dtype=torch.float32)
+        vlens_d = torch.tensor(vlens, device=self.dev, dtype=torch.int32)
+        ts = self.time_each(lambda: api.lt_prefill_attn_lse_lazy_varlen(vq, vk, vv, vout, vlse, vlens_d, vw.S, vw.R,
+                                                                        vw.W, vrows, vratio, 0.0, self.stream),
+                            self.K)
+        v_ms = median(ts)
+        v_fl = sum(prefill_flop(1, vw.Hq, n, vw.D) + lazy_flop(1, vw.Hq, n, vw.D, vw.S, vw.R, vw.W) for n in vlens)
+        log(f"varlen prefill: {v_ms:.3f} ms, {v_fl / v_ms / 1e9:.1f} TFLOP/s")
+        return {"workload": f"qwen32k-varlen: B4 prompts of {', '.join(map(str, vlens))} tokens padded to {vw.N}, "
+                            f"Hq{vw.Hq} Hkv{vw.Hkv} D{vw.D} bf16, sink keys x3, S{vw.S} R{vw.R} W{vw.W}; "
+                            "prefill+LSE+lazy ratio",
+                "ms_median": round(v_ms, 4), "tflops": round(v_fl / v_ms / 1e9, 2),
+                "frac_mfma_peak": round(v_fl / v_ms / 1e9 * 1e12 / PEAK_BF16, 4), "flop": v_fl}
+
+    # -- hybrid decode -------------------------------------------------------
+    def decode_leg(self, varlen=True):
+        torch, api, ops, synth = self.torch, self.api, self.ops, self.synth
+        dw = self.workload(synth.DECODE100K)
+        L = int(dw.extra["layers"])
+        nfull = int(dw.extra["full_layers"])
+        log("allocating the 64-layer hybrid KV cache on device")
+        qs, ks_, vs_, outs, lses, lens = [], [], [], [], [], []
+        for l in range(L):
+            ql, kl, vl = synth.decode_layer(l, dw, device=self.dev)
+            qs.append(ql); ks_.append(kl); vs_.append(vl); lens.append(kl.shape[2])
+            outs.append(torch.empty_like(ql))
+            lses.append(torch.empty(dw.B, dw.Hq, device=self.dev, dtype=torch.float32))
+        ws = ops.decode_workspace(dw.B, dw.Hq, dw.Hkv, dw.D, max(lens), self.dev)
+        torch.cuda.synchronize()
+        bytes_step = sum(2 * dw.B * dw.Hkv * n * dw.D * 2 + 2 * dw.B * dw.Hq * dw.D * 2 for n in lens)
+
+        def decode_all(st):
+            for l in range(L):
+                api.lt_hybrid_decode_attn(qs[l], ks_[l], vs_[l], lens[l], outs[l], lses[l], ws, 0.0, st)
+
+        cap = torch.cuda.Stream()
+
+        def graph_of(fn):
+            cap.wait_stream(self.stream)
+            with torch.cuda.stream(cap):
+                fn(cap)  # eager warm call on the capture stream
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                fn(cap)
+            torch.cuda.synchronize()
+            return g
+
+        graph = graph_of(decode_all)
+        log("decode graph captured")
+        ts = self.time_each(graph.replay, self.K, warm=3)
+        d_ms = median(ts)
+        gbps = bytes_step / (d_ms * 1e-3) / 1e9
+        log(f"decode: {d_ms:.3f} ms/step, {gbps:.1f} GB/s")
+        res = {"decode": {"workload": f"decode100k: B{dw.B}, context {dw.N}, {L} layers Hq{dw.Hq} Hkv{dw.Hkv} "
+                                      f"D{dw.D} bf16, {nfull} full ({dw.N} rows) + {L - nfull} streaming "
+                                      f"({lens[-1]} rows)",
+                          "ms_per_step_median": round(d_ms, 4), "ms_per_step_mean": round(sum(ts) / len(ts), 4),
+                          "gbps": round(gbps, 1), "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
+                          "bytes_per_step": bytes_step, "replays": len(ts)}}
+        del graph
+        if varlen:
+            dlens = synth.DECODE100K_VARLEN_LENS
+            full_lens = torch.tensor(dlens, device=self.dev, dtype=torch.int32)
+            stream_lens = torch.tensor([min(n, lens[-1]) for n in dlens], device=self.dev, dtype=torch.int32)
+            vbytes = sum(sum(2 * dw.Hkv * min(n, lens[l]) * dw.D * 2 for n in dlens) + 2 * dw.B * dw.Hq * dw.D * 2
+                         for l in range(L))
+
+            def decode_all_varlen(st):
+                for l in range(L):
+                    api.lt_hybrid_decode_attn_varlen(qs[l], ks_[l], vs_[l], full_lens if l < nfull else stream_lens,
+                                                     lens[l], outs[l], lses[l], ws, 0.0, st)
+
+            vgraph = graph_of(decode_all_varlen)
+            vts = self.time_each(vgraph.replay, self.K, warm=3)
+            vd_ms = median(vts)
+            vgbps = vbytes / (vd_ms * 1e-3) / 1e9
+            log(f"varlen decode: {vd_ms:.3f} ms/step, {vgbps:.1f} GB/s")
+            res["decode_varlen"] = {
+                "workload": "decode100k-varlen: the decode100k step with contexts "
+                            f"{dlens[0]}, {dlens[1]}, ..., {dlens[-1]} on the full layers (per-sequence lengths on "
+                            f"the device), {lens[-1]} on the streaming ones",
+                "ms_per_step_median": round(vd_ms, 4), "gbps": round(vgbps, 1),
+                "frac_hbm_peak": round(vgbps * 1e9 / PEAK_HBM, 4), "bytes_per_step": vbytes}
+            del vgraph
+        del qs, ks_, vs_, outs, lses, ws
+        torch.cuda.empty_cache()
+        return res
+
+    # -- measured peaks ---------------------------------------------------------
+    def probes_leg(self):
+        torch, api = self.torch, self.api
+
+        def best_ms(fn, reps=3):
+            return min(self.time_each(fn, reps, warm=1))
+
+        blocks, iters = 2048, 20000   # about 10 ms: long enough for the clock the chip holds under load
+        psink = torch.empty(blocks * 256, device=self.dev, dtype=torch.float32)
+        pfl = float(blocks) * 4 * iters * 8 * 16384
+        mfma_ms = best_ms(lambda: api.lt_probe_mfma_bf16(blocks, iters, psink, self.stream))
+        rbuf = torch.empty(4 << 30, device=self.dev, dtype=torch.uint8)
+        rsink = torch.zeros(8192, device=self.dev, dtype=torch.int32)
+        read_ms = best_ms(lambda: api.lt_probe_read(rbuf, 8192, rsink, self.stream))
+        res = {"mfma_bf16_tflops": round(pfl / (mfma_ms * 1e-3) / 1e12, 1),
+               "hbm_read_gbps": round(rbuf.numel() / (read_ms * 1e-3) / 1e9, 1),
+               "spec_mfma_bf16_tflops": PEAK_BF16 / 1e12, "spec_hbm_gbps": PEAK_HBM / 1e9,
+               "probes": "lt_probe_mfma_bf16: 2048 workgroups x 4 waves, 8 independent 16x16x32 bf16 MFMA chains "
+                         "per wave on pseudo-random unit-size register operands, 20000 iterations; lt_probe_read: "
+                         "one pass of 16-byte nontemporal loads over 4 GiB (contiguous share per workgroup), 8192 "
+                         "workgroups; best of 3"}
+        log(f"measured peaks: {res['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, {res['hbm_read_gbps']} GB/s read")
+        del rbuf, rsink, psink
+        torch.cuda.empty_cache()
+        return res
+
+    # -- the 64-layer driver ------------------------------------------------------
+    def driver_leg(self, offline=True, cpu=True):
+        torch, synth = self.torch, self.synth
+        from kv_cache_compression_causal_amd import driver
+        dw = self.workload(synth.DRIVER64)
+        L64, C = int(dw.extra["layers"]), int(dw.extra["capacity"])
+        log(f"driver64: generating the {L64} layers' inputs in HBM")
+        layers = []
+        for l in range(L64):
+            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=self.dev)
+            layers.append((ql, kl, vl))
+        torch.cuda.synchronize()
+        layer_inputs = lambda l: layers[l]
+        fl_layer = prefill_flop(dw.B, dw.Hq, dw.N, dw.D) + lazy_flop(dw.B, dw.Hq, dw.N, dw.D, dw.S, dw.R, dw.W)
+        MiB = 1 << 20
+        # a short untimed pass (warm code paths and allocator), then the timed pass
+        driver.run(layer_inputs, min(4, L64), min(2, C), dw.S, dw.R, dw.W)
+        log("driver64: timed pass")
+        res = driver.run(layer_inputs, L64, C, dw.S, dw.R, dw.W, timing=True)
+        srt = sorted(res.layer_score)
+        out = {
+            "workload": f"driver64: {L64} layers of B{dw.B} N{dw.N} Hq{dw.Hq} Hkv{dw.Hkv} D{dw.D} bf16 (inputs "
+                        f"resident in HBM), per-layer sink scale and recency bias, queue capacity {C}, "
+                        f"S{dw.S} R{dw.R} W{dw.W}",
+            "wall_s": round(res.wall_s, 4),
+            "tflops_whole_pass": round(L64 * fl_layer / res.wall_s / 1e12, 2),
+            "frac_mfma_peak_whole_pass": round(L64 * fl_layer / res.wall_s / PEAK_BF16, 4),
+            "what_is_timed": "every layer's prefill+LSE+lazy ratio, its ratios to the host (a sync per layer), "
+                             "the library's queue push and the compaction of each evicted layer",
+            "prefill_ms_mean": round(sum(res.prefill_ms) / len(res.prefill_ms), 4),
+            "prefill_ms_median": round(median(res.prefill_ms), 4),
+            "streaming_layers": [l for l in range(L64) if res.is_streaming[l]],
+            "evicted_at_step": res.evicted_at_step,
+            "score_min": min(res.layer_score), "score_max": max(res.layer_score),
+            "min_adjacent_score_gap": min(b - a for a, b in zip(srt, srt[1:])) if L64 > 1 else None,
+            "kv_all_full_MiB": L64 * res.full_bytes / MiB,
+            "kv_retained_final_MiB": res.retained_bytes[-1] / MiB,
+            "kv_peak_transient_MiB": max(res.transient_bytes) / MiB,
+        }
+        log(f"driver64: {res.wall_s:.3f} s whole pass ({out['tflops_whole_pass']} TFLOP/s), retained "
+            f"{out['kv_retained_final_MiB']:.0f} MiB of {out['kv_all_full_MiB']:.0f}, "
+            f"peak {out['kv_peak_transient_MiB']:.0f} MiB")
+        gpu_ratio = {l: res.head_ratio[l] for l in (0, L64 - 1)}
+        del res
+        res_b = driver.run(layer_inputs, L64, C, dw.S, dw.R, dw.W, timing=True,
+                           policy=self._lib.LT_EVICT_BEFORE_PUSH)
+        out["evict_before_push"] = {
+            "wall_s": round(res_b.wall_s, 4),
+            "streaming_layers": [l for l in range(L64) if res_b.is_streaming[l]],
+            "evicted_at_step": res_b.evicted_at_step,
+            "kv_retained_final_MiB": res_b.retained_bytes[-1] / MiB,
+            "kv_peak_transient_MiB": max(res_b.transient_bytes) / MiB,
+        }
+        del res_b
+        res_e = driver.run(layer_inputs, L64, C, dw.S, dw.R, dw.W, timing=True, emit=True)
+        base = out["evicted_at_step"]
+        out["emitted_slices"] = {
+            "wall_s": round(res_e.wall_s, 4),
+            "same_selection": res_e.evicted_at_step == base,
+            "compaction_launches": 0,
+            "kv_retained_final_MiB": res_e.retained_bytes[-1] / MiB,
+            "kv_peak_transient_MiB": max(res_e.transient_bytes) / MiB,
+            "prefill_ms_mean": round(sum(res_e.prefill_ms) / len(res_e.prefill_ms), 4),
+        }
+        del res_e
+        log(f"driver64: evict-before-push {out['evict_before_push']['wall_s']} s, emitted slices "
+            f"{out['emitted_slices']['wall_s']} s")
+        if cpu:
+            out["oracle"] = self.driver_oracle(dw, layers, gpu_ratio, fl_layer)
+        del layers
+        torch.cuda.empty_cache()
+        if offline:
+            out_off = self.offline_leg(dw)
+        else:
+            out_off = None
+        return out, out_off
+
+    def driver_oracle(self, dw, layers, gpu_ratio, fl_layer):
+        """The oracle on layers 0 and L-1 of the driver: every head's last W
+        rows (what the lazy ratios and so the selection need), timed and
+        extrapolated by FLOP to the whole 64-layer pass (x32 per layer)."""
+        import numpy as np
+        import oracle
+        L64 = int(dw.extra["layers"])
+        G = dw.Hq // dw.Hkv
+        pos = np.arange(dw.N - dw.W, dw.N, dtype=np.int32)
+        t_cpu, fl, err = 0.0, 0.0, 0.0
+        for l in (0, L64 - 1):
+            q, k, v = layers[l]
+            for hk in range(dw.Hkv):
+                kh = k[0, hk].double().cpu().numpy()
+                vh = v[0, hk].double().cpu().numpy()
+                for h in range(hk * G, (hk + 1) * G):
+                    qr = q[0, h, dw.N - dw.W:].double().cpu().numpy()
+                    c0 = time.perf_counter()
+                    r = oracle.rows(kh, vh, pos, qr, S=dw.S, R=dw.R, lazy=True, streaming=False)
+                    t_cpu += time.perf_counter() - c0
+                    fl += sum(4.0 * dw.D * (int(p) + 1) + 2.0 * dw.D * min(dw.S + dw.R, int(p) + 1) for p in pos)
+                    err = max(err, abs(float(r["lazy"].mean()) - gpu_ratio[l][h]))
+        est = t_cpu * (L64 * fl_layer / (2 * fl))
+        log(f"driver64 oracle: {t_cpu:.1f} s on the last W rows of layers 0 and {L64 - 1} "
+            f"({fl / t_cpu / 1e9:.2f} GFLOP/s); whole-pass estimate {est / 3600:.1f} h")
+        return {"layers": [0, L64 - 1], "sample": f"the last W={dw.W} rows of all {dw.Hq} heads of each layer "
+                                                  f"(what the lazy ratios need), fp64",
+                "seconds": round(t_cpu, 2), "gflops": round(fl / t_cpu / 1e9, 3),
+                "whole_pass_estimate_s": round(est, 1),
+                "whole_pass_estimate": "the measured FLOP rate applied to 64 full layers (x32 per measured layer)",
+                "max_abs_ratio_diff_vs_gpu": err, "threads": oracle.threads()}
+
+    def offline_leg(self, dw):
+        torch, synth = self.torch, self.synth
+        from kv_cache_compression_causal_amd import driver
+        L64, C = int(dw.extra["layers"]), int(dw.extra["capacity"])
+        P_off = 4
+        log(f"running offline selection over {P_off} prompts")
+
+        def prompt_inputs(p, l):
+            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=self.dev, prompt=p)
+            return ql, kl, vl
+
+        off = driver.offline(prompt_inputs, P_off, L64, C, dw.S, dw.R, dw.W, timing=True)
+        fl = prefill_flop(dw.B, dw.Hq, dw.N, dw.D) + lazy_flop(dw.B, dw.Hq, dw.N, dw.D, dw.S, dw.R, dw.W)
+        med_ms = median(off.prefill_ms)
+        res = {
+            "workload": f"offline4: {P_off} synthetic prompts through the {L64} driver layers (per-layer sink "
+                        f"scale and recency bias shared by all prompts), mean layer score over prompts, capacity {C}",
+            "streaming_layers": [l for l in range(L64) if off.is_streaming[l]],
+            "differs_from_test_time": [sum(a != b for a, b in zip(off.is_streaming, tt))
+                                       for tt in off.test_time_streaming],
+            "prefill_launches": len(off.prefill_ms),
+            "prefill_ms_median": round(med_ms, 4),
+            "prefill_tflops": round(fl / (med_ms * 1e-3) / 1e12, 2),
+            "wall_s_with_input_generation": round(off.wall_s, 2),
+        }
+        log(f"offline4: {res['prefill_tflops']} TFLOP/s per launch, layers differing from each prompt's "
+            f"test-time choice: {res['differs_from_test_time']}")
+        del off
+        torch.cuda.empty_cache()
+        return res
+
+    # -- the oracle on a row sample of a prefill workload ---------------------------
+    def cpu_prefill(self, w, q, k, v, nrow):
+        import numpy as np
+        import oracle
+        torch = self.torch
+        log(f"timing the oracle on a {nrow}-row sample of {w.name}")
+        B, N, Hq, Hkv, D, S, R, W = w.B, w.N, w.Hq, w.Hkv, w.D, w.S, w.R, w.W
+        rng = np.random.default_rng(0)
+        G = Hq // Hkv
+        heads = rng.integers(0, Hq, size=nrow)
+        pos = np.concatenate([np.arange(N - W, N), rng.integers(0, N, size=max(0, nrow - W))])[:nrow]
+        kh_cache = {}
+        flop, t_cpu = 0.0, 0.0
+        for h in sorted(set(int(x) for x in heads)):
+            sel = np.nonzero(heads == h)[0]
+            hk = h // G
+            if hk not in kh_cache:
+                kh_cache[hk] = (k[0, hk].double().cpu().numpy(), v[0, hk].double().cpu().numpy())
+            kh, vh = kh_cache[hk]
+            ps = pos[sel].astype(np.int32)
+            qr = q[0, h].index_select(0, torch.as_tensor(ps, device=self.dev, dtype=torch.long)).double().cpu().numpy()
+            c0 = time.perf_counter()
+            oracle.rows(kh, vh, ps, qr, S=S, R=R, lazy=True, streaming=False)
+            t_cpu += time.perf_counter() - c0
+            flop += sum(4.0 * D * (int(p) + 1) for p in ps)
+            flop += sum(2.0 * D * min(S + R, int(p) + 1) for p in ps if p >= N - W)
+        tf = flop / t_cpu / 1e12
+        log(f"oracle: {tf * 1e3:.3f} GFLOP/s on {oracle.threads()} threads ({t_cpu:.1f} s)")
+        return {"value": round(tf, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+                "cpu_model": cpu_model(),
+                "sample": f"{nrow} query rows of the {w.name} layer (the last W={W} rows + uniform random rows, "
+                          f"random heads), full softmax row materialised in fp64; {t_cpu:.1f} s; FLOP counted as "
+                          f"for the GPU (4*D*(i+1) per row + lazy numerator)"}
+
+    def cpu_decode(self):
+        import oracle
+        synth = self.synth
+        dw = self.workload(synth.DECODE100K)
+        nfull = int(dw.extra["full_layers"])
+        t_layer, b_layer = {}, {}
+        for l in (0, nfull):
+            ql, kl, vl = synth.decode_layer(l, dw, device=self.dev)
+            qh = ql[:1].double().cpu().numpy()
+            kh = kl[:1].double().cpu().numpy()
+            vh = vl[:1].double().cpu().numpy()
+            del ql, kl, vl
+            c0 = time.perf_counter()
+            oracle.decode(qh, kh, vh)
+            t_layer[l] = time.perf_counter() - c0
+            b_layer[l] = 2 * dw.Hkv * kh.shape[2] * dw.D * 2 + 2 * dw.Hq * dw.D * 2
+            del qh, kh, vh
+        L = int(dw.extra["layers"])
+        t_step = dw.B * (nfull * t_layer[0] + (L - nfull) * t_layer[nfull])
+        b_step = dw.B * (nfull * b_layer[0] + (L - nfull) * b_layer[nfull])
+        log(f"oracle decode: {b_step / t_step / 1e9:.3f} GB/s")
+        return {"value": round(b_step / t_step / 1e9, 3), "unit": "GB/s", "cores": oracle.threads(),
+                "kind": "oracle",
+                "sample": f"decode100k layers 0 ({dw.N} rows) and {nfull} (S+R rows), batch element 0, fp64 "
+                          f"({t_layer[0]:.2f} s + {t_layer[nfull]:.3f} s), extrapolated to the 64-layer step "
+                          f"at B{dw.B}"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", choices=CONFIGS, default="all")
+    ap.add_argument("--S", type=int, default=None, help="sink keys (every workload measured)")
+    ap.add_argument("--R", type=int, default=None, help="recent keys (every workload measured)")
+    ap.add_argument("--wobs", type=int, default=None, help="observed last queries W (prefill workloads)")
+    ap.add_argument("--seed", type=int, default=None, help="base seed of the synthetic inputs")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-driver", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=98304,
-                    help="rows of the oracle's CPU sample")
+                    help="rows of the oracle's CPU sample of the headline prefill")
     ap.add_argument("--copy-only", type=int, default=0, metavar="BYTES",
                     help="only run a device-to-device copy of BYTES, 5 times (the reference "
                          "kernel that scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
@@ -97,10 +684,9 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
-    from kv_cache_compression_causal_amd import _lib, api, ops, synth
+    from kv_cache_compression_causal_amd import _lib, synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -118,487 +704,136 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copied {args.copy_only} bytes x5")
         return 0
-    K, Wm = args.steps, args.warmup
-    w = synth.QWEN32K
-    B, N, Hq, Hkv, D, S, R, W = w.B, w.N, w.Hq, w.Hkv, w.D, w.S, w.R, w.W
+    bench = Bench(args, torch, dev)
+    cfg = args.config
+    overrides = {k: getattr(args, k) for k in ("S", "R", "wobs", "seed") if getattr(args, k) is not None}
+    result = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "data": "synthetic"}
+    extra = {}
 
-    log(f"generating {w.name} inputs on device")
-    q, k, v = synth.workload_qkv(w, device=dev)
-    out = torch.empty_like(q)
-    lse = torch.empty(B, Hq, N, device=dev, dtype=torch.float32)
-    rows = torch.empty(B, Hq, W, device=dev, dtype=torch.float32)
-    ratio = torch.empty(B, Hq, device=dev, dtype=torch.float32)
-    srows = min(N, S + R)
-    k_st = torch.empty(B, Hkv, srows, D, device=dev, dtype=q.dtype)
-    v_st = torch.empty_like(k_st)
-    sout = torch.empty_like(q)
-    slse = torch.empty_like(lse)
-    total_layers = K + Wm
-    queue = api.LazyQueue(total_layers, total_layers // 2)
-    stream = torch.cuda.current_stream()
-    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    layer = [0]
-    # Each layer's ratios go to the host through one of two pinned buffers, so
-    # that layer l's queue push (and the compaction it may trigger) runs while
-    # layer l+1's prefill is on the GPU: the next prefill does not depend on
-    # the queue's decision, only the KV bookkeeping does.
-    ratio_d = [ratio, torch.empty_like(ratio)]
-    ratio_h = [torch.empty(B, Hq, dtype=torch.float32, pin_memory=True) for _ in range(2)]
-    copied = [torch.cuda.Event() for _ in range(2)]
-    pending = [None]
-
-    def finish(slot):
-        copied[slot].synchronize()  # the per-layer device->host hand-off of the method
-        score = float(ratio_h[slot].double().mean())
-        evicted = queue.push(layer[0], score)
-        layer[0] += 1
-        if evicted >= 0:
-            # one resident layer stands in for every layer: compact it
-            api.lt_compact_kv_streaming(k, v, k_st, v_st, S, R, stream)
-
-    def step(i, timed_idx=None):
-        slot = i % 2
-        if timed_idx is not None:
-            ev0[timed_idx].record(stream)
-        api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio_d[slot], 0.0, stream)
-        if timed_idx is not None:
-            ev1[timed_idx].record(stream)
-        ratio_h[slot].copy_(ratio_d[slot], non_blocking=True)
-        copied[slot].record(stream)
-        if pending[0] is not None:
-            finish(pending[0])
-        pending[0] = slot
-
-    def drain():
-        if pending[0] is not None:
-            finish(pending[0])
-            pending[0] = None
-
-    log("warmup")
-    for i in range(Wm):
-        step(i)
-    drain()
-    torch.cuda.synchronize()
-    log(f"timing {K} steps")
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(i, i)
-    drain()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / K
-    kern_ms = sum(a.elapsed_time(b) for a, b in zip(ev0, ev1)) / K
-    fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
-    value = fl / (ms_step * 1e-3) / 1e12
-    achieved = fl / (kern_ms * 1e-3) / 1e12
-    log(f"prefill+lazy: {ms_step:.3f} ms/step, kernel {kern_ms:.3f} ms, {achieved:.1f} TFLOP/s")
-    queue.close()
-
-    # plain prefill (W = 0) for the lazy-ratio overhead
-    def timed(fn, reps):
-        for _ in range(Wm):
-            fn()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    # Two variants compared under the same clock: launches alternate between
-    # them (A B B A ...), each timed by its own events, and the comparison is
-    # the median over neighbouring pairs, so that a clock that drifts or dips
-    # during the measurement weighs on both alike.
-    def paired(fa, fb, reps):
-        for _ in range(Wm):
-            fa()
-            fb()
-        torch.cuda.synchronize()
-        ev = []
-        for r in range(reps):
-            pair = {}
-            for which in ((0, 1) if r % 2 == 0 else (1, 0)):
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                (fa if which == 0 else fb)()
-                b.record(stream)
-                pair[which] = (a, b)
-            ev.append(pair)
-        torch.cuda.synchronize()
-        ta = [p[0][0].elapsed_time(p[0][1]) for p in ev]
-        tb = [p[1][0].elapsed_time(p[1][1]) for p in ev]
-        rel = sorted((y - x) / x for x, y in zip(ta, tb))
-        med = lambda xs: sorted(xs)[len(xs) // 2]
-        return med(ta), med(tb), 100.0 * rel[len(rel) // 2]
-
-    run_plain = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, 0, None, None, 0.0, stream)
-    run_lazy = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, stream)
-    # the same step writing the layer's streaming slice from the prefill itself
-    run_emit = lambda: api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, k_st, v_st,
-                                                         None, 0.0, stream)
-    plain_ms, lazy_ms, lazy_pct = paired(run_plain, run_lazy, K)
-    log(f"plain prefill: {plain_ms:.3f} ms, with the lazy ratio: {lazy_ms:.3f} ms ({lazy_pct:+.2f}%)")
-    lazy2_ms, emit_ms, emit_pct = paired(run_lazy, run_emit, K)
-    log(f"prefill writing the streaming slice: {emit_ms:.3f} ms (without: {lazy2_ms:.3f} ms, {emit_pct:+.2f}%)")
-    st_ms = timed(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, stream), K)
-    st_fl = streaming_flop(B, Hq, N, D, S, R)
-    log(f"streaming: {st_ms:.3f} ms, {st_fl / st_ms / 1e9:.1f} TFLOP/s")
-
-    result = {
-        "metric": "prefill attn+lazy-ratio TFLOP/s @32K (% MFMA peak); hybrid decode HBM GB/s",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": K,
-        "warmup": Wm,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "qwen32k layer: B1 N32768 Hq40 Hkv8 D128 bf16, sink keys x3, "
-                               "S4 R1020 W128; step = prefill+LSE+lazy ratio, ratio D2H, "
-                               "queue push, KV compaction (a layer's hand-off overlaps the next "
-                               "layer's prefill)",
-                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
-        "prefill_lazy": {"kernel_ms": round(kern_ms, 4), "tflops": round(achieved, 2),
-                         "frac_mfma_peak": round(achieved * 1e12 / PEAK_BF16, 4),
-                         "flop_per_launch": fl},
-        # with and without the lazy ratio, launches alternated (A B B A ...):
-        # the median over neighbouring pairs of the relative difference
-        "lazy_overhead_pct": round(lazy_pct, 3),
-        "prefill_emit": {"ms": round(emit_ms, 4), "ms_without_slice": round(lazy2_ms, 4),
-                         "overhead_pct": round(emit_pct, 3),
-                         "what": "prefill+LSE+lazy ratio also writing the 4 MiB sink+recent KV slice "
-                                 "(replaces the compaction kernel)"},
-        "prefill_plain": {"ms": round(plain_ms, 4),
-                          "tflops": round(prefill_flop(B, Hq, N, D) / plain_ms / 1e9, 2)},
-        "streaming": {"ms": round(st_ms, 4), "tflops": round(st_fl / st_ms / 1e9, 2),
-                      "flop": st_fl},
-    }
-
-    src = os.path.join(ROOT, "kv_cache_compression_causal_amd", "csrc", "attn_bf16.hip")
-    traffic = traffic_from_profile(src, os.path.join(ROOT, "profiles", "prefill_lazy_qwen32k_pmc.txt"))
-    result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
-                          "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4),
-                          "traffic": traffic,
-                          "kernel": "attn_bf16_kernel<D=128, RB=3, BT=128, FULL_LAZY> + lazy_reduce_kernel"}
-    del sout, slse
-
-    # Variable-length batch: four prompts of 32K, 24K, 16K and 8K tokens padded to 32K.
-    if not args.no_varlen:
-        vw, vlens = synth.QWEN32K_VARLEN, synth.QWEN32K_VARLEN_LENS
-        log("generating the variable-length batch")
-        vq, vk, vv = synth.workload_qkv(vw, device=dev)
-        vout = torch.empty_like(vq)
-        vlse = torch.empty(vw.B, vw.Hq, vw.N, device=dev, dtype=torch.float32)
-        vrows = torch.empty(vw.B, vw.Hq, vw.W, device=dev, dtype=torch.float32)
-        vratio = torch.empty(vw.B, vw.Hq, device=dev, dtype=torch.float32)
-        vlens_d = torch.tensor(vlens, device=dev, dtype=torch.int32)
-        v_ms = timed(lambda: api.lt_prefill_attn_lse_lazy_varlen(vq, vk, vv, vout, vlse, vlens_d, vw.S, vw.R,
-                                                                 vw.W, vrows, vratio, 0.0, stream), K)
-        v_fl = sum(prefill_flop(1, vw.Hq, n, vw.D) + lazy_flop(1, vw.Hq, n, vw.D, vw.S, vw.R, vw.W)
-                   for n in vlens)
-        result["prefill_varlen"] = {
-            "workload": "qwen32k-varlen: B4 prompts of 32768, 24576, 16384, 8192 tokens padded to 32768, "
-                        "Hq40 Hkv8 D128 bf16, sink keys x3, S4 R1020 W128; prefill+LSE+lazy ratio",
-            "ms": round(v_ms, 4), "tflops": round(v_fl / v_ms / 1e9, 2),
-            "frac_mfma_peak": round(v_fl / v_ms / 1e9 * 1e12 / PEAK_BF16, 4), "flop": v_fl}
-        log(f"varlen prefill: {v_ms:.3f} ms, {v_fl / v_ms / 1e9:.1f} TFLOP/s")
-        del vq, vk, vv, vout, vlse, vrows, vratio
+    def prefill_workload_leg(w, headline, emit):
+        log(f"generating {w.name} inputs on device")
+        q, k, v = synth.workload_qkv(w, device=dev)
+        step = bench.step_leg(w, q, k, v) if headline else None
+        legs = bench.prefill_leg(w, q, k, v, emit=emit)
+        cpu = None
+        if headline and not args.no_cpu:
+            cpu = bench.cpu_prefill(w, q, k, v, args.cpu_rows if w.N >= 32768 else args.cpu_rows // 4)
+        del q, k, v
         torch.cuda.empty_cache()
+        return step, legs, cpu
 
-    # hybrid decode step: B8, context 100000, 64 layers (32 full + 32 streaming)
-    if not args.no_decode:
-        dw = synth.DECODE100K
-        L = int(dw.extra["layers"])
-        nfull = int(dw.extra["full_layers"])
-        log("allocating the 64-layer hybrid KV cache on device")
-        qs, ks_, vs_, outs, lses, lens = [], [], [], [], [], []
-        for l in range(L):
-            ql, kl, vl = synth.decode_layer(l, dw, device=dev)
-            qs.append(ql); ks_.append(kl); vs_.append(vl); lens.append(kl.shape[2])
-            outs.append(torch.empty_like(ql))
-            lses.append(torch.empty(dw.B, dw.Hq, device=dev, dtype=torch.float32))
-        ws = ops.decode_workspace(dw.B, dw.Hq, dw.Hkv, dw.D, max(lens), dev)
-        torch.cuda.synchronize()
-        bytes_step = sum(2 * dw.B * dw.Hkv * n * dw.D * 2 + 2 * dw.B * dw.Hq * dw.D * 2 for n in lens)
+    def step_fields(w, step, what):
+        return {"value": round(step["value"], 2), "unit": "TFLOP/s", "ms_per_step": round(step["ms_per_step"], 4),
+                "dtype": "bf16",
+                "config": {"workload": f"{w.name} layer: B{w.B} N{w.N} Hq{w.Hq} Hkv{w.Hkv} D{w.D} bf16"
+                                       f"{', sink keys x3' if w.sink_scale != 1.0 else ''}, S{w.S} R{w.R} W{w.W}, "
+                                       f"seed {w.seed}; step = {what}",
+                           "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+                           **({"overrides": overrides} if overrides else {})}}
 
-        def decode_all(st):
-            for l in range(L):
-                api.lt_hybrid_decode_attn(qs[l], ks_[l], vs_[l], lens[l], outs[l], lses[l], ws, 0.0, st)
+    step_what = ("prefill+LSE+lazy ratio, ratio D2H, queue push (layer score in the library), KV compaction "
+                 "(a layer's hand-off overlaps the next layer's prefill)")
 
-        cap = torch.cuda.Stream()
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            decode_all(cap)  # eager warm call on the capture stream
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=cap):
-            decode_all(cap)
-        torch.cuda.synchronize()
-        log("decode graph captured")
-        for _ in range(Wm):
-            graph.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(K):
-            graph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        d_ms = a.elapsed_time(b) / K
-        gbps = bytes_step / (d_ms * 1e-3) / 1e9
-        log(f"decode: {d_ms:.3f} ms/step, {gbps:.1f} GB/s")
-        result["decode"] = {"workload": "decode100k: B8, context 100000, 64 layers Hq40 Hkv8 D128 "
-                                        "bf16, 32 full (100000 rows) + 32 streaming (1024 rows)",
-                            "ms_per_step": round(d_ms, 4), "gbps": round(gbps, 1),
-                            "frac_hbm_peak": round(gbps * 1e9 / PEAK_HBM, 4),
-                            "bytes_per_step": bytes_step}
-        del graph
-        # The same step with eight different contexts on the full layers.
+    if cfg in ("all", "qwen32k", "mistral8k"):
+        w = bench.workload(synth.QWEN32K if cfg != "mistral8k" else synth.MISTRAL8K)
+        step, legs, cpu = prefill_workload_leg(w, True, emit=True)
+        result.update(step_fields(w, step, step_what))
+        achieved = step["flop"] / (step["kernel_ms_mean"] * 1e-3) / 1e12
+        alt = legs["prefill_lazy"]
+        # the headline workload's legs at the top level; the kernel time is
+        # the mean over the timed steps' launches (the roofline's), the
+        # median of the launches alternated with the plain prefill beside it
+        legs["prefill_lazy"] = {"kernel_ms": round(step["kernel_ms_mean"], 4),
+                                "kernel_ms_median": round(step["kernel_ms_median"], 4),
+                                "tflops": round(achieved, 2), "frac_mfma_peak": round(achieved * 1e12 / PEAK_BF16, 4),
+                                "flop_per_launch": step["flop"], "ms_median_alternated": alt["ms_median"],
+                                "frac_mfma_peak_alternated": alt["frac_mfma_peak"]}
+        result["headline_workload"] = w.name
+        extra.update(legs)
+        src = os.path.join(ROOT, "kv_cache_compression_causal_amd", "csrc", "attn_bf16.hip")
+        traffic = traffic_from_profile(src, os.path.join(ROOT, "profiles", f"prefill_lazy_{w.name}_pmc.txt"))
+        result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16 / 1e12,
+                              "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_BF16, 4), "traffic": traffic,
+                              "kernel": "attn_bf16_kernel<D=128, FULL_LAZY> + lazy_reduce_kernel",
+                              "launches": args.steps,
+                              "what": "algorithmic FLOP per launch / mean launch duration (HIP events on the launch "
+                                      "stream, the timed steps)"}
+        if cpu is not None:
+            result["cpu_baseline"] = cpu
+    if cfg == "all":
+        extra["tiny"] = bench.tiny_leg(cpu=not args.no_cpu)
+        w2 = bench.workload(synth.MISTRAL8K)
+        _, legs2, _ = prefill_workload_leg(w2, False, emit=False)
+        extra["mistral8k"] = legs2
         if not args.no_varlen:
-            dlens = synth.DECODE100K_VARLEN_LENS
-            full_lens = torch.tensor(dlens, device=dev, dtype=torch.int32)
-            stream_lens = torch.tensor([min(n, lens[-1]) for n in dlens], device=dev, dtype=torch.int32)
-            vbytes = sum(sum(2 * dw.Hkv * min(n, lens[l]) * dw.D * 2 for n in dlens) + 2 * dw.B * dw.Hq * dw.D * 2
-                         for l in range(L))
-
-            def decode_all_varlen(st):
-                for l in range(L):
-                    api.lt_hybrid_decode_attn_varlen(qs[l], ks_[l], vs_[l], full_lens if l < nfull else stream_lens,
-                                                     lens[l], outs[l], lses[l], ws, 0.0, st)
-
-            with torch.cuda.stream(cap):
-                decode_all_varlen(cap)
-            torch.cuda.synchronize()
-            vgraph = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(vgraph, stream=cap):
-                decode_all_varlen(cap)
-            torch.cuda.synchronize()
-            for _ in range(Wm):
-                vgraph.replay()
-            torch.cuda.synchronize()
-            a.record(stream)
-            for _ in range(K):
-                vgraph.replay()
-            b.record(stream)
-            torch.cuda.synchronize()
-            vd_ms = a.elapsed_time(b) / K
-            vgbps = vbytes / (vd_ms * 1e-3) / 1e9
-            log(f"varlen decode: {vd_ms:.3f} ms/step, {vgbps:.1f} GB/s")
-            result["decode_varlen"] = {
-                "workload": "decode100k-varlen: the decode100k step with contexts 100000, 87500, ..., 12500 "
-                            "on the full layers (per-sequence lengths on the device), 1024 on the streaming ones",
-                "ms_per_step": round(vd_ms, 4), "gbps": round(vgbps, 1),
-                "frac_hbm_peak": round(vgbps * 1e9 / PEAK_HBM, 4), "bytes_per_step": vbytes}
-            del vgraph
-        del qs, ks_, vs_, outs, lses, ws
-        torch.cuda.empty_cache()
-
-    # Measured peaks: the matrix-core and HBM-read rates the chip delivers in
-    # practice (probe kernels of the library), next to the published peaks the
-    # roofline fractions use.
-    def best_ms(fn, reps=3):
-        fn()
-        torch.cuda.synchronize()
-        best = float("inf")
-        for _ in range(reps):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            best = min(best, e0.elapsed_time(e1))
-        return best
-
-    blocks, iters = 2048, 20000   # about 10 ms: long enough for the clock the chip holds under load
-    psink = torch.empty(blocks * 256, device=dev, dtype=torch.float32)
-    pfl = float(blocks) * 4 * iters * 8 * 16384
-    mfma_ms = best_ms(lambda: api.lt_probe_mfma_bf16(blocks, iters, psink, stream))
-    rbuf = torch.empty(4 << 30, device=dev, dtype=torch.uint8)
-    rsink = torch.zeros(8192, device=dev, dtype=torch.int32)
-    read_ms = best_ms(lambda: api.lt_probe_read(rbuf, 8192, rsink, stream))
-    result["measured_peaks"] = {
-        "mfma_bf16_tflops": round(pfl / (mfma_ms * 1e-3) / 1e12, 1),
-        "hbm_read_gbps": round(rbuf.numel() / (read_ms * 1e-3) / 1e9, 1),
-        "spec_mfma_bf16_tflops": PEAK_BF16 / 1e12, "spec_hbm_gbps": PEAK_HBM / 1e9,
-        "probes": "lt_probe_mfma_bf16: 2048 workgroups x 4 waves, 8 independent 16x16x32 bf16 "
-                  "MFMA chains per wave on pseudo-random unit-size register operands, 20000 iterations; "
-                  "lt_probe_read: one pass of 16-byte nontemporal loads over 4 GiB (contiguous share per "
-                  "workgroup), 8192 workgroups; best of 3"}
-    mp = result["measured_peaks"]
-    # the headline kernels against what this machine delivers, next to the spec fractions
-    mp["prefill_lazy_frac_of_measured_mfma"] = round(achieved / mp["mfma_bf16_tflops"], 4)
-    if "decode" in result:
-        mp["decode_frac_of_measured_read"] = round(result["decode"]["gbps"] / mp["hbm_read_gbps"], 4)
-    log(f"measured peaks: {result['measured_peaks']['mfma_bf16_tflops']} TFLOP/s bf16 MFMA, "
-        f"{result['measured_peaks']['hbm_read_gbps']} GB/s read")
-    del rbuf, rsink, psink
-    torch.cuda.empty_cache()
-
-    # The 64-layer LightTransfer-Test prefill: selection and KV bytes
-    if not args.no_driver:
-        from kv_cache_compression_causal_amd import driver
-        dw = synth.DRIVER64
-        log("running the 64-layer driver")
-
-        def layer_inputs(l):
-            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=dev)
-            return ql, kl, vl
-
-        res = driver.run(layer_inputs, int(dw.extra["layers"]), int(dw.extra["capacity"]), dw.S, dw.R,
-                         dw.W, timing=True)
-        srt = sorted(res.layer_score)
-        MiB = 1 << 20
-        L64 = res.layers
-        result["driver64"] = {
-            "workload": "driver64: 64 layers of the qwen32k shape, per-layer sink scale and recency "
-                        "bias, queue capacity 32, S4 R1020 W128",
-            "streaming_layers": [l for l in range(L64) if res.is_streaming[l]],
-            "evicted_at_step": res.evicted_at_step,
-            "kv_all_full_MiB": L64 * res.full_bytes / MiB,
-            "kv_retained_final_MiB": res.retained_bytes[-1] / MiB,
-            "kv_peak_transient_MiB": max(res.transient_bytes) / MiB,
-            "min_adjacent_score_gap": min(b - a for a, b in zip(srt, srt[1:])),
-            "prefill_ms_mean": round(sum(res.prefill_ms) / len(res.prefill_ms), 4),
-        }
-        log(f"driver64: retained {res.retained_bytes[-1] / MiB:.0f} MiB of {L64 * res.full_bytes / MiB:.0f}, "
-            f"peak {max(res.transient_bytes) / MiB:.0f} MiB")
-        torch.cuda.empty_cache()
-        # The other eviction timing the pages describe: the laziest queued layer
-        # leaves before the current one is stored.
-        res_b = driver.run(layer_inputs, int(dw.extra["layers"]), int(dw.extra["capacity"]), dw.S, dw.R,
-                           dw.W, timing=False, policy=_lib.LT_EVICT_BEFORE_PUSH)
-        result["driver64"]["evict_before_push"] = {
-            "streaming_layers": [l for l in range(L64) if res_b.is_streaming[l]],
-            "evicted_at_step": res_b.evicted_at_step,
-            "kv_retained_final_MiB": res_b.retained_bytes[-1] / MiB,
-            "kv_peak_transient_MiB": max(res_b.transient_bytes) / MiB,
-        }
-        log(f"driver64 (evict before push): peak {max(res_b.transient_bytes) / MiB:.0f} MiB")
-        del res_b
-        torch.cuda.empty_cache()
-        # Slices written by each layer's prefill: no compaction launches.
-        res_e = driver.run(layer_inputs, int(dw.extra["layers"]), int(dw.extra["capacity"]), dw.S, dw.R,
-                           dw.W, timing=True, emit=True)
-        result["driver64"]["emitted_slices"] = {
-            "same_selection": res_e.evicted_at_step == res.evicted_at_step,
-            "compaction_launches": 0,
-            "kv_retained_final_MiB": res_e.retained_bytes[-1] / MiB,
-            "kv_peak_transient_MiB": max(res_e.transient_bytes) / MiB,
-            "prefill_ms_mean": round(sum(res_e.prefill_ms) / len(res_e.prefill_ms), 4),
-        }
-        log(f"driver64 (emitted slices): peak {max(res_e.transient_bytes) / MiB:.0f} MiB")
-        del res_e
-        torch.cuda.empty_cache()
-        # Offline selection: the same layers on several prompts, mean score, top half streaming.
-        P_off = 4
-        log(f"running offline selection over {P_off} prompts")
-
-        def prompt_inputs(p, l):
-            ql, kl, vl, _, _ = synth.driver_layer(l, dw, device=dev, prompt=p)
-            return ql, kl, vl
-
-        off = driver.offline(prompt_inputs, P_off, L64, int(dw.extra["capacity"]), dw.S, dw.R, dw.W,
-                             timing=True)
-        off_flop = prefill_flop(dw.B, dw.Hq, dw.N, dw.D) + lazy_flop(dw.B, dw.Hq, dw.N, dw.D, dw.S, dw.R,
-                                                                    dw.W)
-        mean_ms = sum(off.prefill_ms) / len(off.prefill_ms)
-        result["offline4"] = {
-            "workload": "offline4: 4 synthetic prompts through the 64 driver layers (per-layer sink scale "
-                        "and recency bias shared by all prompts), mean layer score over prompts, capacity 32",
-            "streaming_layers": [l for l in range(L64) if off.is_streaming[l]],
-            "differs_from_test_time": [sum(a != b for a, b in zip(off.is_streaming, tt))
-                                       for tt in off.test_time_streaming],
-            "prefill_launches": len(off.prefill_ms),
-            "prefill_ms_mean": round(mean_ms, 4),
-            "prefill_tflops": round(off_flop / (mean_ms * 1e-3) / 1e12, 2),
-            "wall_s": round(off.wall_s, 2),
-        }
-        log(f"offline4: {result['offline4']['prefill_tflops']} TFLOP/s per launch, layers differing from "
-            f"each prompt's test-time choice: {result['offline4']['differs_from_test_time']}")
-        del off
-        torch.cuda.empty_cache()
-
-    # CPU baseline: the oracle on a bounded row sample of the same workload
-    if not args.no_cpu:
-        import oracle
-        log("timing the oracle on a row sample")
-        nrow = args.cpu_rows
-        rng = np.random.default_rng(0)
-        G = Hq // Hkv
-        heads = rng.integers(0, Hq, size=nrow)
-        pos = np.concatenate([np.arange(N - W, N), rng.integers(0, N, size=nrow - W)])[:nrow]
-        kh_cache = {}
-        flop = 0.0
-        t_cpu = 0.0
-        for h in sorted(set(int(x) for x in heads)):
-            sel = np.nonzero(heads == h)[0]
-            hk = h // G
-            if hk not in kh_cache:
-                kh_cache[hk] = (k[0, hk].double().cpu().numpy(), v[0, hk].double().cpu().numpy())
-            kh, vh = kh_cache[hk]
-            ps = pos[sel].astype(np.int32)
-            qr = q[0, h].index_select(0, torch.as_tensor(ps, device=dev, dtype=torch.long)).double().cpu().numpy()
-            c0 = time.perf_counter()
-            oracle.rows(kh, vh, ps, qr, S=S, R=R, lazy=True, streaming=False)
-            t_cpu += time.perf_counter() - c0
-            flop += sum(4.0 * D * (int(p) + 1) for p in ps)
-            flop += sum(2.0 * D * min(S + R, int(p) + 1) for p in ps if p >= N - W)
-        cpu_tflops = flop / t_cpu / 1e12
-        cpu_model = "unknown"
-        try:
-            with open("/proc/cpuinfo") as f:
-                for line in f:
-                    if line.startswith("model name"):
-                        cpu_model = line.split(":", 1)[1].strip()
-                        break
-        except OSError:
-            pass
-        result["cpu_baseline"] = {"value": round(cpu_tflops, 6), "unit": "TFLOP/s",
-                                  "cores": oracle.threads(), "kind": "oracle", "cpu_model": cpu_model,
-                                  "sample": f"{nrow} query rows of the qwen32k layer (the last W=128 rows "
-                                            f"+ uniform random rows, random heads), full softmax row "
-                                            f"materialised in fp64; {t_cpu:.1f} s; FLOP counted as "
-                                            f"for the GPU (4*D*(i+1) per row + lazy numerator)"}
-        log(f"oracle: {cpu_tflops * 1e3:.3f} GFLOP/s on {oracle.threads()} threads ({t_cpu:.1f} s)")
-        if not args.no_decode:
-            # The oracle's decode: batch element 0 of one full and one streaming
-            # layer of the decode step, extrapolated to the 64-layer step (x8
-            # batch, x32 layers of each kind); bytes counted as for the GPU.
-            dw = synth.DECODE100K
-            nfull = int(dw.extra["full_layers"])
-            t_layer, b_layer = {}, {}
-            for l in (0, nfull):
-                ql, kl, vl = synth.decode_layer(l, dw, device=dev)
-                qh = ql[:1].double().cpu().numpy()
-                kh = kl[:1].double().cpu().numpy()
-                vh = vl[:1].double().cpu().numpy()
-                del ql, kl, vl
-                c0 = time.perf_counter()
-                oracle.decode(qh, kh, vh)
-                t_layer[l] = time.perf_counter() - c0
-                b_layer[l] = 2 * dw.Hkv * kh.shape[2] * dw.D * 2 + 2 * dw.Hq * dw.D * 2
-                del qh, kh, vh
-            L = int(dw.extra["layers"])
-            t_step = dw.B * (nfull * t_layer[0] + (L - nfull) * t_layer[nfull])
-            b_step = dw.B * (nfull * b_layer[0] + (L - nfull) * b_layer[nfull])
-            result["cpu_baseline"]["decode"] = {
-                "value": round(b_step / t_step / 1e9, 3), "unit": "GB/s",
-                "sample": f"decode100k layers 0 (100000 rows) and {nfull} (1024 rows), batch element 0, "
-                          f"fp64 ({t_layer[0]:.2f} s + {t_layer[nfull]:.3f} s), extrapolated to "
-                          f"the 64-layer step at B8"}
-            log(f"oracle decode: {b_step / t_step / 1e9:.3f} GB/s")
-
+            extra["qwen32k_varlen"] = bench.varlen_leg()
+    if cfg == "tiny":
+        t = bench.tiny_leg(cpu=not args.no_cpu)
+        w = bench.workload(synth.TINY)
+        extra["tiny"] = t
+        ms = t["latency_us_median"] * 1e-3
+        result.update({"value": t["tflops"], "unit": "TFLOP/s", "ms_per_step": round(ms, 5), "dtype": "f32",
+                       "config": {"workload": t["workload"] + "; step = one prefill+LSE+lazy ratio launch "
+                                                             "(median of 100, each timed by its own events)",
+                                  "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+                                  **({"overrides": overrides} if overrides else {})}})
+        result["roofline"] = {"bound": "alu", "achieved": t["tflops"], "peak": PEAK_F32_VALU / 1e12,
+                              "unit": "TFLOP/s", "frac": round(t["tflops"] * 1e12 / PEAK_F32_VALU, 6),
+                              "traffic": None, "kernel": "attn_f32_kernel<D=64, FULL_LAZY> + lazy_reduce_kernel",
+                              "what": "latency-bound: a handful of workgroups"}
+        if "oracle_full_ms" in t:
+            result["cpu_baseline"] = {"value": round(t["flop"] / (t["oracle_full_ms"] * 1e-3) / 1e12, 6),
+                                      "unit": "TFLOP/s", "cores": t["oracle_threads"], "kind": "oracle",
+                                      "cpu_model": cpu_model(),
+                                      "sample": "the whole tiny layer (full oracle, incl. streaming outputs)"}
+    if cfg in ("all", "decode100k") and not args.no_decode:
+        dres = bench.decode_leg(varlen=not args.no_varlen)
+        extra.update(dres)
+        if cfg == "decode100k":
+            d = dres["decode"]
+            result.update({"value": d["gbps"], "unit": "GB/s", "ms_per_step": d["ms_per_step_median"],
+                           "dtype": "bf16",
+                           "config": {"workload": d["workload"] + "; step = one decode token through the 64 layers "
+                                                                  "(a replayed HIP graph), median of replays",
+                                      "global_batch": 8, "seq_len": 100000, "parallelism": "none (1 GPU)",
+                                      **({"overrides": overrides} if overrides else {})}})
+            result["roofline"] = {"bound": "hbm", "achieved": d["gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                                  "frac": d["frac_hbm_peak"], "traffic": None,
+                                  "kernel": "decode_bf16_kernel<D=128> + decode_combine_kernel (64 layers)"}
+            if not args.no_cpu:
+                result["cpu_baseline"] = bench.cpu_decode()
+        elif not args.no_cpu and "cpu_baseline" in result:
+            result["cpu_baseline"]["decode"] = bench.cpu_decode()
+    if cfg == "all":
+        mp = bench.probes_leg()
+        mp["prefill_lazy_frac_of_measured_mfma"] = round(result["roofline"]["achieved"] / mp["mfma_bf16_tflops"], 4)
+        if "decode" in extra:
+            mp["decode_frac_of_measured_read"] = round(extra["decode"]["gbps"] / mp["hbm_read_gbps"], 4)
+        extra["measured_peaks"] = mp
+    if cfg in ("all", "driver64") and not args.no_driver:
+        drv, off = bench.driver_leg(offline=(cfg == "all"), cpu=not args.no_cpu)
+        extra["driver64"] = drv
+        if off is not None:
+            extra["offline4"] = off
+        if cfg == "driver64":
+            w = bench.workload(synth.DRIVER64)
+            result.update({"value": drv["tflops_whole_pass"], "unit": "TFLOP/s",
+                           "ms_per_step": round(drv["wall_s"] * 1e3 / int(w.extra["layers"]), 4), "dtype": "bf16",
+                           "config": {"workload": drv["workload"] + "; step = one layer of the timed 64-layer pass",
+                                      "global_batch": w.B, "seq_len": w.N, "parallelism": "none (1 GPU)",
+                                      **({"overrides": overrides} if overrides else {})}})
+            result["roofline"] = {"bound": "mfma", "achieved": drv["tflops_whole_pass"],
+                                  "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                                  "frac": drv["frac_mfma_peak_whole_pass"], "traffic": None,
+                                  "kernel": "attn_bf16_kernel<D=128, FULL_LAZY> (64 launches) with the per-layer "
+                                            "sync and queue"}
+            if "oracle" in drv:
+                o = drv["oracle"]
+                result["cpu_baseline"] = {"value": round(o["gflops"] / 1e3, 6), "unit": "TFLOP/s",
+                                          "cores": o["threads"], "kind": "oracle", "cpu_model": cpu_model(),
+                                          "sample": o["sample"] + " of layers 0 and 63"}
+    result.update(extra)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -20,7 +20,10 @@ def _sample_rows(N, W, n_rand, seed):
     return np.array(sorted(rows), dtype=np.int32)
 
 
-def _check_prefill_workload(w, n_rand, heads=None):
+def _check_prefill_workload(w, n_rand, heads=None, n_rand_other=0):
+    """Every head's last W rows (the lazy ratio's rows) and first 64 rows;
+    n_rand seeded random rows more for the heads in ``heads`` (all if None),
+    n_rand_other for the rest."""
     print(f"workload {w.name}: generating on device", flush=True)
     q, k, v = synth.workload_qkv(w, device=DEV)
     out, lse, rows, ratio = ops.prefill(q, k, v, w.S, w.R, w.W)
@@ -31,8 +34,9 @@ def _check_prefill_workload(w, n_rand, heads=None):
     want_ratio = np.empty((w.B, w.Hq))
     for b in range(w.B):
         kh = {hk: (np64(k[b, hk]), np64(v[b, hk])) for hk in range(w.Hkv)}
-        for h in (range(w.Hq) if heads is None else heads):
-            pos = _sample_rows(w.N, w.W, n_rand, seed=1000 * b + h)
+        for h in range(w.Hq):
+            nr = n_rand if heads is None or h in heads else n_rand_other
+            pos = _sample_rows(w.N, w.W, nr, seed=1000 * b + h)
             qr = np64(q[b, h][torch.as_tensor(pos, device=DEV, dtype=torch.long)])
             r = oracle.rows(kh[h // G][0], kh[h // G][1], pos, qr, S=w.S, R=w.R)
             pt = torch.as_tensor(pos, device=DEV, dtype=torch.long)
@@ -53,7 +57,7 @@ def test_mistral8k_full_size():
 
 
 def test_qwen32k_full_size():
-    ratio = _check_prefill_workload(synth.QWEN32K, n_rand=32, heads=list(range(0, 40, 3)))
+    ratio = _check_prefill_workload(synth.QWEN32K, n_rand=32, heads=list(range(0, 40, 3)), n_rand_other=4)
     assert np.all((ratio >= 0) & (ratio <= 1))
 
 
@@ -112,6 +116,35 @@ def test_decode100k_varlen_full_size():
         assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
 
 
+def _check_selection_end_to_end(want_scores, got_scores, evicted, is_streaming, capacity, policy):
+    """The selection made on the GPU's ratios against the oracle's fp64 layer
+    scores.  Every GPU score is within the ratio tolerance of the oracle's.
+    When no two oracle scores are within twice the tolerance, the eviction
+    order must be the oracle's own; otherwise (near ties, where the bf16
+    path may rank two layers either way) the decisions must still be
+    consistent with the oracle's scores up to that margin: no layer kept at
+    full size scores more than 2 x tolerance above a streaming one (the last
+    layer, which the pop-before-push timing always keeps, excepted).  Which
+    of the two applied is printed."""
+    tol = TOL_BF16_RATIO
+    assert max(abs(a - b) for a, b in zip(want_scores, got_scores)) <= tol
+    srt = sorted(want_scores)
+    gap = min(b - a for a, b in zip(srt, srt[1:]))
+    if gap > 2 * tol:
+        print(f"end-to-end selection: exact (minimum score gap {gap:.3g})", flush=True)
+        ev2, _ = oracle.select_lazy_layers(want_scores, capacity, policy=policy)
+        assert ev2 == evicted
+        return
+    L = len(want_scores)
+    cand = range(L - 1) if policy == "before" else range(L)
+    kept = [want_scores[l] for l in cand if not is_streaming[l]]
+    gone = [want_scores[l] for l in cand if is_streaming[l]]
+    print(f"end-to-end selection: minimum score gap {gap:.3g} <= 2 x {tol}; checked up to that margin "
+          f"(kept max {max(kept) if kept else None}, streaming min {min(gone) if gone else None})", flush=True)
+    if kept and gone:
+        assert max(kept) <= min(gone) + 2 * tol
+
+
 @pytest.mark.parametrize("policy", ["after", "before"])
 def test_driver_small_stack(policy):
     """8 layers with the driver's sink/recency recipe at N=1024: per-layer ratios
@@ -142,11 +175,8 @@ def test_driver_small_stack(policy):
     assert gpu_scores == res.layer_score
     ev, st = oracle.select_lazy_layers(gpu_scores, 4, policy=policy)
     assert ev == res.evicted_at_step and st == res.is_streaming
-    # (ii) end to end with the oracle's own ratios, when no two scores are within tolerance
-    srt = sorted(want_scores)
-    if min(b - a for a, b in zip(srt, srt[1:])) > 2 * TOL_BF16_RATIO:
-        ev2, _ = oracle.select_lazy_layers(want_scores, 4, policy=policy)
-        assert ev2 == res.evicted_at_step
+    # (ii) end to end against the oracle's own fp64 scores
+    _check_selection_end_to_end(want_scores, res.layer_score, res.evicted_at_step, res.is_streaming, 4, policy)
     acc = oracle.kv_accounting(res.evicted_at_step, res.full_bytes, res.stream_bytes, policy=policy)
     assert acc["retained"] == res.retained_bytes and acc["transient"] == res.transient_bytes
     full, stream = oracle.kv_bytes(1, 2, 1024, 128, 2, w.S, w.R)
@@ -212,8 +242,83 @@ def test_offline_selection_small_stack():
     assert mean == res.layer_score and st == res.is_streaming
     for p in range(P):
         assert oracle.select_lazy_layers(gpu[p], C)[1] == res.test_time_streaming[p]
-    # (ii) end to end with the oracle's own ratios, when no two means are within tolerance
+    # (ii) end to end with the oracle's own ratios: the same set when no two
+    # means are within tolerance, else consistent with them up to that margin
     mean_ref, st_ref = oracle.select_offline(want, C)
+    assert max(abs(a - b) for a, b in zip(mean_ref, res.layer_score)) <= TOL_BF16_RATIO
     srt = sorted(mean_ref)
-    if min(b - a for a, b in zip(srt, srt[1:])) > 2 * TOL_BF16_RATIO:
+    gap = min(b - a for a, b in zip(srt, srt[1:]))
+    if gap > 2 * TOL_BF16_RATIO:
+        print(f"offline selection end to end: exact (minimum gap {gap:.3g})", flush=True)
         assert st_ref == res.is_streaming
+    else:
+        print(f"offline selection end to end: minimum gap {gap:.3g}, checked up to 2 x tolerance", flush=True)
+        kept = [mean_ref[l] for l in range(Lyr) if not res.is_streaming[l]]
+        gone = [mean_ref[l] for l in range(Lyr) if res.is_streaming[l]]
+        assert max(kept) <= min(gone) + 2 * TOL_BF16_RATIO
+
+
+def test_driver64_full_size():
+    """The 64-layer, 32K-token driver (qwen32k-shaped layers, per-layer sink
+    scale and recency bias, capacity 32) as the bench runs it, once per
+    eviction timing:
+      (i) the 64 x 40 fp32 ratios of the GPU through the oracle's queue give
+          the driver's eviction order bit for bit, and the oracle's KV
+          accounting gives its per-step bytes;
+     (ii) the ratios of layers 0 and 63 and of the two layers whose scores
+          are closest, every head (its last W rows), against the fp64
+          oracle, and the selection against the oracle's scores end to end.
+    Both runs see the same prefill results: their ratios must agree bit for
+    bit."""
+    from kv_cache_compression_causal_amd import _lib
+    w = synth.DRIVER64
+    L, C = int(w.extra["layers"]), int(w.extra["capacity"])
+    G = w.Hq // w.Hkv
+
+    def inputs(l):
+        q, k, v, _, _ = synth.driver_layer(l, w, device=DEV)
+        return q, k, v
+
+    runs = {}
+    for policy, lt_policy in (("after", _lib.LT_EVICT_AFTER_PUSH), ("before", _lib.LT_EVICT_BEFORE_PUSH)):
+        print(f"driver64, eviction {policy} push: {L} layers", flush=True)
+        res = driver.run(inputs, L, C, w.S, w.R, w.W, policy=lt_policy)
+        torch.cuda.empty_cache()
+        gpu_scores = [oracle.layer_score(np.array(r, dtype=np.float32).astype(np.float64)) for r in res.head_ratio]
+        assert gpu_scores == res.layer_score
+        ev, st = oracle.select_lazy_layers(gpu_scores, C, policy=policy)
+        assert ev == res.evicted_at_step and st == res.is_streaming
+        assert sum(st) == L - C
+        acc = oracle.kv_accounting(res.evicted_at_step, res.full_bytes, res.stream_bytes, policy=policy)
+        assert acc["retained"] == res.retained_bytes and acc["transient"] == res.transient_bytes
+        runs[policy] = res
+    assert runs["after"].head_ratio == runs["before"].head_ratio
+    MiB = 1 << 20
+    assert runs["after"].retained_bytes[-1] == 4224 * MiB
+    assert runs["before"].retained_bytes[-1] == 4224 * MiB
+    ratios = runs["after"].head_ratio
+    scores = runs["after"].layer_score
+    order = sorted(range(L), key=lambda l: scores[l])
+    i_tie = min(range(L - 1), key=lambda i: scores[order[i + 1]] - scores[order[i]])
+    check_layers = sorted({0, L - 1, order[i_tie], order[i_tie + 1]})
+    want = {}
+    pos = np.arange(w.N - w.W, w.N, dtype=np.int32)
+    for l in check_layers:
+        print(f"driver64 layer {l}: oracle on every head's last {w.W} rows", flush=True)
+        q, k, v = inputs(l)
+        hr = []
+        for hk in range(w.Hkv):
+            kh, vh = np64(k[0, hk]), np64(v[0, hk])
+            for h in range(hk * G, (hk + 1) * G):
+                r = oracle.rows(kh, vh, pos, np64(q[0, h, w.N - w.W:]), S=w.S, R=w.R, streaming=False)
+                hr.append(r["lazy"].sum() / w.W)
+        del q, k, v
+        np.testing.assert_allclose(np.array(ratios[l]), np.array(hr), atol=TOL_BF16_RATIO, rtol=0)
+        want[l] = oracle.layer_score(hr)
+        assert abs(want[l] - scores[l]) <= TOL_BF16_RATIO
+    # the closest pair: their order on the GPU may differ from the oracle's
+    # only if the oracle's scores are within twice the tolerance
+    a, b = order[i_tie], order[i_tie + 1]
+    print(f"closest layer scores: {a} {scores[a]!r} / {b} {scores[b]!r} (oracle {want[a]!r} / {want[b]!r})",
+          flush=True)
+    assert want[a] <= want[b] + 2 * TOL_BF16_RATIO
