@@ -34,6 +34,7 @@
 // sequences of different lengths, interleaving them (most of the first
 // workgroups then exit at once) ran at half the rate.
 
+#include <atomic>
 #include <type_traits>
 
 #include "lt_internal.h"
@@ -305,15 +306,24 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     };
     // O^T += V^T P^T for keys [32h, 32h+32) of a staged V tile; the V^T
     // fragments of block db+3 are read while the products of block db run.
+    // Streaming: the swizzled chunk of 16-dim block db is chunk(0) ^ 2db, so
+    // the lane's V^T offsets are one base XOR a per-block constant.
+    const int vt_row = 4 * g + (c16 >> 2);
+    const int vt_base = vt_row * D + swz_v<D>(vt_row, (c16 & 3) >> 1) * 8 + (c16 & 1) * 4;
     auto pv = [&](const bf16 *Vb, int h, const bf16x8 (&pk)[RB], f32x4 (&o)[RB][DB]) {
         const int row1 = BN * h + 4 * g + (c16 >> 2), row2 = row1 + 16;
         const int half = (c16 & 1) * 4;
         bf16x8 A[DB];
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            const int lch = 2 * db + ((c16 & 3) >> 1);
-            A[db] = concat(lds_read_tr(Vb + row1 * D + swz_v<D>(row1, lch) * 8 + half),
-                           lds_read_tr(Vb + row2 * D + swz_v<D>(row2, lch) * 8 + half));
+            if (MODE == MODE_STREAM) {
+                const int off = (vt_base ^ (16 * db)) + BN * h * D;
+                A[db] = concat(lds_read_tr(Vb + off), lds_read_tr(Vb + off + 16 * D));
+            } else {
+                const int lch = 2 * db + ((c16 & 3) >> 1);
+                A[db] = concat(lds_read_tr(Vb + row1 * D + swz_v<D>(row1, lch) * 8 + half),
+                               lds_read_tr(Vb + row2 * D + swz_v<D>(row2, lch) * 8 + half));
+            }
         }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -509,11 +519,30 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (it < n_iter) run_tile(it, std::integral_constant<int, 0>{});
 
     // Finalize: O / l, LSE = (m + log2 l) * ln 2, lazy row = lz / l.
+    // Streaming goes through the (now idle) LDS tile buffers: each wave
+    // writes its 16*RB normalized rows into a region of its own and stores
+    // them back 16 bytes per lane, every wave-wide store covering whole rows
+    // (stored straight from the matrix-core layout, each store instruction
+    // writes 8-byte pieces of 16 rows, which costs a short streaming window a
+    // few per cent).
+    bf16 *const ostage = lds + wave * WROWS * D;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
         const float lt = group_sum(l[rb]);
         const float inv = 1.f / lt;
-        if (pos[rb] < N) {
+        if (MODE == MODE_STREAM) {
+            const int row = rb * 16 + c16;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                bf16x4 w;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) w[r] = (bf16)(o[rb][db][r] * inv);
+                const int ch = (2 * db + (g >> 1)) ^ (row & (CPR - 1));
+                *(bf16x4 *)(ostage + row * D + ch * 8 + (g & 1) * 4) = w;
+            }
+            if (a.lse != nullptr && g == 0 && pos[rb] < N)
+                a.lse[((int64_t)b * a.Hq + head[rb]) * a.N + pos[rb]] = (m[rb] + __log2f(lt)) * kLn2;
+        } else if (pos[rb] < N) {
             bf16 *op = (bf16 *)a.o + b * a.o_sb + (int64_t)head[rb] * a.o_sh +
                        (int64_t)pos[rb] * a.o_sn + 4 * g;
 #pragma unroll
@@ -530,6 +559,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
             const float zt = group_sum(lz[rb]);
             if (g == 0 && pos[rb] < N && pos[rb] >= N - a.W)
                 a.lazy_rows[((int64_t)b * a.Hq + head[rb]) * a.W + (pos[rb] - (N - a.W))] = zt * inv;
+        }
+    }
+
+    if (MODE == MODE_STREAM) {
+        // Read back whole rows: lane l takes chunk l % CPR of row
+        // RPI * u + l / CPR; row r of the wave is query position r / G,
+        // head r % G (positions advance by carrying the head index).  The
+        // region is the wave's own and a wave's LDS accesses run in order;
+        // lanes read what other lanes wrote, so the reads must stay below
+        // the writes.
+        asm volatile("" ::: "memory");
+        const int ch = lane % CPR;
+        const int r = rw0 + lane / CPR;
+        int p = r / G, hh = r - p * G;
+#pragma unroll
+        for (int u = 0; u < WROWS / RPI; ++u) {
+            const int row = RPI * u + lane / CPR;
+            const bf16x8 v = *(const bf16x8 *)(ostage + row * D + (ch ^ (row & (CPR - 1))) * 8);
+            if (p < N)
+                *(bf16x8 *)((bf16 *)a.o + b * a.o_sb + (int64_t)(hk * G + hh) * a.o_sh + (int64_t)p * a.o_sn +
+                            ch * 8) = v;
+            hh += RPI;
+            while (hh >= G) {
+                hh -= G;
+                ++p;
+            }
         }
     }
 
@@ -594,6 +649,19 @@ hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+// Compute units of the current device (cached per device).
+int cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+        cache[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D>
 hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
     // 3 row blocks per wave: O (3*D/16 x 4), S^T (3 x 8), Q^T (3*D/16 x 2)
@@ -603,8 +671,14 @@ hipError_t launch_d(AttnArgs a, int mode, hipStream_t st) {
     // 64 keys to fit its registers, in 4-wave workgroups: a window of about
     // S + R keys is short work next to the workgroup's own Q loads and O
     // stores, and with two workgroups per CU one computes while the other
-    // waits on memory.
+    // waits on memory.  Full attention over a grid of fewer than four 8-wave
+    // workgroups per CU (an 8K-token layer: 688 on 256 CUs) takes the
+    // 4-wave, 64-key shape too: twice the workgroups even out the causal
+    // triangle's tail (2-3% faster there; at 32K tokens the 8-wave shape is).
     if (mode == MODE_STREAM) return launch_cfg<D, 3, 64, 4, 1 << MODE_STREAM>(a, mode, st);
+    const int64_t items8 = ((int64_t)a.N * a.G + 383) / 384 * a.B * a.Hkv;
+    if (items8 < 4 * cu_count())
+        return launch_cfg<D, 3, 64, 4, (1 << MODE_FULL) | (1 << MODE_FULL_LAZY)>(a, mode, st);
     return launch_cfg<D, 3, 128, 8, (1 << MODE_FULL) | (1 << MODE_FULL_LAZY)>(a, mode, st);
 }
 

@@ -53,6 +53,34 @@ def test_prefill_lse_lazy(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
     assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], tr)
 
 
+@pytest.mark.parametrize("D", [128, 64])
+def test_prefill_large_grid_shape(D):
+    """A grid of at least four 8-wave workgroups per CU (here 1024 on 256
+    CUs) runs the 8-wave, 128-key shape (smaller grids, as in the cases
+    above, take the 4-wave, 64-key one): out, LSE, the lazy rows and the
+    ratio on sampled rows of every head against the oracle, a ragged tail
+    included.  The streaming kernel on the same tensors too."""
+    B, N, Hq, Hkv, S, R, W = 1, 6140, 64, 8, 4, 300, 48
+    print(f"large-grid prefill D{D} B{B} N{N} Hq{Hq} Hkv{Hkv}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, 31 + D, torch.bfloat16, device=DEV)
+    out, lse, rows, ratio = ops.prefill(q, k, v, S, R, W)
+    sout, slse = ops.streaming(q, k, v, S, R)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    rng = np.random.default_rng(D)
+    for h in range(Hq):
+        pos = np.unique(np.concatenate([np.arange(N - W, N), np.arange(0, 8), rng.integers(0, N, 6)])).astype(np.int32)
+        pt = torch.as_tensor(pos, device=DEV, dtype=torch.long)
+        r = oracle.rows(np64(k[0, h // G]), np64(v[0, h // G]), pos, np64(q[0, h][pt]), S=S, R=R)
+        assert_close(f"out h{h}", np64(out[0, h][pt]), r["out"], TOL_BF16_OUT)
+        assert_close(f"lse h{h}", np64(lse[0, h][pt]), r["lse"], TOL_BF16_LSE)
+        assert_close(f"stream out h{h}", np64(sout[0, h][pt]), r["sout"], TOL_BF16_OUT)
+        assert_close(f"stream lse h{h}", np64(slse[0, h][pt]), r["slse"], TOL_BF16_LSE)
+        obs = pos >= N - W
+        assert_close(f"lazy rows h{h}", np64(rows[0, h]), r["lazy"][obs], TOL_BF16_RATIO)
+        assert abs(float(ratio[0, h]) - r["lazy"][obs].mean()) <= TOL_BF16_RATIO
+
+
 @pytest.mark.parametrize("B,N,Hq,Hkv,D,dtype,S,R,W,seed", PREFILL_CASES)
 def test_prefill_plain_matches_lazy_variant(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
     """W = 0 runs the kernel without the epilogue: out and lse are bit-identical."""
