@@ -2,7 +2,7 @@
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
                 [--config {all,tiny,mistral8k,qwen32k,driver64,decode100k}]
-                [--S S] [--R R] [--wobs W_obs] [--seed SEED]
+                [--reps N] [--S S] [--R R] [--wobs W_obs] [--seed SEED]
                 [--no-decode] [--no-driver] [--no-cpu] [--no-varlen]
 
 Default (--config all): one JSON line whose headline is the qwen32k layer
@@ -118,6 +118,7 @@ class Bench:
         self.dev = dev
         self.K = args.steps
         self.Wm = args.warmup
+        self.reps = args.reps if args.reps is not None else args.steps  # timed launches of a per-launch leg
         self.stream = torch.cuda.current_stream()
         from kv_cache_compression_causal_amd import _lib, api, ops, synth
         self._lib, self.api, self.ops, self.synth = _lib, api, ops, synth
@@ -264,7 +265,7 @@ class Bench:
         st = self.stream
         run_plain = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, 0, None, None, 0.0, st)
         run_lazy = lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, st)
-        plain_ms, lazy_ms, lazy_pct = self.paired(run_plain, run_lazy, self.K)
+        plain_ms, lazy_ms, lazy_pct = self.paired(run_plain, run_lazy, self.reps)
         fl = prefill_flop(B, Hq, N, D) + lazy_flop(B, Hq, N, D, S, R, W)
         pfl = prefill_flop(B, Hq, N, D)
         res = {
@@ -283,7 +284,7 @@ class Bench:
             v_st = torch.empty_like(k_st)
             run_emit = lambda: api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, k_st,
                                                                  v_st, None, 0.0, st)
-            base_ms, emit_ms, emit_pct = self.paired(run_lazy, run_emit, self.K)
+            base_ms, emit_ms, emit_pct = self.paired(run_lazy, run_emit, self.reps)
             res["prefill_emit"] = {"ms_median": round(emit_ms, 4), "ms_without_slice": round(base_ms, 4),
                                    "overhead_pct": round(emit_pct, 3),
                                    "what": "prefill+LSE+lazy ratio also writing the sink+recent KV slice "
@@ -292,7 +293,7 @@ class Bench:
             del k_st, v_st
         sout = torch.empty_like(q)
         slse = torch.empty_like(lse)
-        sts = self.time_each(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, st), self.K)
+        sts = self.time_each(lambda: api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, st), self.reps)
         st_ms = median(sts)
         sfl = streaming_flop(B, Hq, N, D, S, R)
         res["streaming"] = {"ms_median": round(st_ms, 4), "ms_mean": round(sum(sts) / len(sts), 4),
@@ -344,7 +345,7 @@ class Bench:
         vlens_d = torch.tensor(vlens, device=self.dev, dtype=torch.int32)
         ts = self.time_each(lambda: api.lt_prefill_attn_lse_lazy_varlen(vq, vk, vv, vout, vlse, vlens_d, vw.S, vw.R,
                                                                         vw.W, vrows, vratio, 0.0, self.stream),
-                            self.K)
+                            self.reps)
         v_ms = median(ts)
         v_fl = sum(prefill_flop(1, vw.Hq, n, vw.D) + lazy_flop(1, vw.Hq, n, vw.D, vw.S, vw.R, vw.W) for n in vlens)
         log(f"varlen prefill: {v_ms:.3f} ms, {v_fl / v_ms / 1e9:.1f} TFLOP/s")
@@ -390,7 +391,7 @@ class Bench:
 
         graph = graph_of(decode_all)
         log("decode graph captured")
-        ts = self.time_each(graph.replay, self.K, warm=3)
+        ts = self.time_each(graph.replay, self.reps, warm=3)
         d_ms = median(ts)
         gbps = bytes_step / (d_ms * 1e-3) / 1e9
         log(f"decode: {d_ms:.3f} ms/step, {gbps:.1f} GB/s")
@@ -414,7 +415,7 @@ class Bench:
                                                      lens[l], outs[l], lses[l], ws, 0.0, st)
 
             vgraph = graph_of(decode_all_varlen)
-            vts = self.time_each(vgraph.replay, self.K, warm=3)
+            vts = self.time_each(vgraph.replay, self.reps, warm=3)
             vd_ms = median(vts)
             vgbps = vbytes / (vd_ms * 1e-3) / 1e9
             log(f"varlen decode: {vd_ms:.3f} ms/step, {vgbps:.1f} GB/s")
@@ -671,6 +672,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", choices=CONFIGS, default="all")
+    ap.add_argument("--reps", type=int, default=None,
+                    help="timed launches of each per-launch leg (default: --steps)")
     ap.add_argument("--S", type=int, default=None, help="sink keys (every workload measured)")
     ap.add_argument("--R", type=int, default=None, help="recent keys (every workload measured)")
     ap.add_argument("--wobs", type=int, default=None, help="observed last queries W (prefill workloads)")

@@ -10,6 +10,7 @@ import ctypes
 import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblt.so")
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblt_debug.so")
 
 LT_OK, LT_ERR_NULL, LT_ERR_SHAPE, LT_ERR_DTYPE, LT_ERR_LAYOUT, LT_ERR_WORKSPACE, LT_ERR_HIP, \
     LT_ERR_VALUE = range(8)
@@ -54,12 +55,18 @@ _lib = None
 def lib() -> ctypes.CDLL:
     """Load liblt.so once; raise if it has not been built."""
     global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+    if _lib is None:
+        _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` (liblt.so, or the LDS-poisoning
+    liblt_debug.so the tests compare with it) with every signature declared."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m kv_cache_compression_causal_amd.build`")
-    L = ctypes.CDLL(LIB_PATH)
+    L = ctypes.CDLL(path)
     c_int, c_int64, c_void_p, c_size_t = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
     fp = ctypes.POINTER(ctypes.c_float)
     L.lt_prefill_attn_lse_lazy.argtypes = [ctypes.POINTER(LtShape), LtView, LtView, LtView, LtView,
@@ -144,7 +151,6 @@ def lib() -> ctypes.CDLL:
     L.lt_probe_mfma_bf16.restype = c_int
     L.lt_probe_read.argtypes = [c_void_p, c_size_t, c_int, c_void_p, c_void_p]
     L.lt_probe_read.restype = c_int
-    _lib = L
     return L
 
 

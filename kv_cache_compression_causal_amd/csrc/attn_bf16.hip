@@ -191,6 +191,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const float c = a.c;
     const int r0 = qt * BROWS;
     if (r0 >= N * G) return;  // past this sequence's end (whole workgroup, before any barrier)
+    poison_lds<64 * NW>(lds, (int)sizeof(lds), tid);
     const int rw0 = r0 + wave * WROWS;
     const int nrows = N * G;
     const int wg_last = ((r0 + BROWS < nrows ? r0 + BROWS : nrows) - 1) / G;  // last position
@@ -628,6 +629,9 @@ hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     a.n_qtiles = (int)((rows + brows - 1) / brows);
     dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv));
     dim3 block(64 * NW);
+    if (log_enabled())
+        log_printf("  launch attn_bf16_kernel<D=%d, RB=%d, BT=%d, mode=%s, NW=%d> grid %u x %u threads", D, RB, BT,
+                   mode == MODE_FULL ? "full" : mode == MODE_FULL_LAZY ? "full+lazy" : "stream", NW, grid.x, block.x);
     if constexpr ((MODES & (1 << MODE_FULL)) != 0) {
         if (mode == MODE_FULL) {
             hipLaunchKernelGGL((attn_bf16_kernel<D, RB, BT, MODE_FULL, NW>), grid, block, 0, st, a);
@@ -691,6 +695,7 @@ hipError_t launch_attn_bf16(const AttnArgs &a, int D, int mode, hipStream_t st) 
 
 hipError_t launch_lazy_reduce(float *lazy_rows, float *lazy_ratio, int BH, int W, const int *seq_len,
                               int Hq, int N, hipStream_t st) {
+    if (log_enabled()) log_printf("  launch lazy_reduce_kernel grid %d x 256 threads", (BH + 255) / 256);
     hipLaunchKernelGGL(lazy_reduce_kernel, dim3((BH + 255) / 256), dim3(256), 0, st, lazy_rows,
                        lazy_ratio, BH, W, seq_len, Hq, N);
     return hipGetLastError();

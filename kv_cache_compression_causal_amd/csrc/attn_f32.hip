@@ -56,6 +56,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
     const int N = seq_length(a.seq_len, b, a.N);
     const int q0 = blockIdx.x * kRows;
     if (q0 >= N) return;  // past this sequence's end (whole workgroup, before any barrier)
+    poison_lds<64 * kWaves>(smem, (int)sizeof(smem), tid);
     const int i = q0 + rl;
     const bool row_ok = i < N;
     const int last_row = (q0 + kRows < N ? q0 + kRows : N) - 1;
@@ -216,6 +217,10 @@ template <int D>
 hipError_t launch_d(const AttnArgs &a, int mode, hipStream_t st) {
     dim3 grid((unsigned)((a.N + kRows - 1) / kRows), (unsigned)(a.B * a.Hq));
     dim3 block(64 * kWaves);
+    if (log_enabled())
+        log_printf("  launch attn_f32_kernel<D=%d, mode=%s> grid %u x %u x %u threads", D,
+                   mode == MODE_FULL ? "full" : mode == MODE_FULL_LAZY ? "full+lazy" : "stream", grid.x, grid.y,
+                   block.x);
     switch (mode) {
     case MODE_FULL:
         hipLaunchKernelGGL((attn_f32_kernel<D, MODE_FULL>), grid, block, 0, st, a);

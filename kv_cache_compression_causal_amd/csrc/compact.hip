@@ -81,6 +81,7 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t st) {
     const int64_t total = (int64_t)a.B * a.Hkv * (a.D * a.elem / 16) * 2;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 1024) blocks = 1024;
+    if (log_enabled()) log_printf("  launch append_kernel grid %lld x 256 threads", (long long)blocks);
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }
@@ -90,6 +91,7 @@ hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
     int64_t blocks = (total + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks < 1) blocks = 1;
+    if (log_enabled()) log_printf("  launch compact_kernel grid %lld x 256 threads", (long long)blocks);
     hipLaunchKernelGGL(compact_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a);
     return hipGetLastError();
 }

@@ -197,6 +197,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int hk = UNIFORM ? (int)(blockIdx.y % a.Hkv) : (int)blockIdx.y;
+    poison_lds<256>(smem, (int)sizeof(smem), tid);
+    poison_lds<256>(red_m, (int)sizeof(red_m), tid);
+    poison_lds<256>(red_l, (int)sizeof(red_l), tid);
     read_now(a.q), read_now(a.k), read_now(a.v), read_now(a.ws);
     read_now(a.k_sb), read_now(a.k_sh), read_now(a.k_sn);
     read_now(a.v_sb), read_now(a.v_sh), read_now(a.v_sn);
@@ -539,6 +542,10 @@ hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
     if (dtype == LT_BF16) {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv))
                               : dim3((unsigned)a.n_parts, (unsigned)a.Hkv);
+        if (log_enabled())
+            log_printf("  launch decode_bf16_kernel<D=%d, %s> grid %u x %u x 256 threads (%s), then "
+                       "decode_combine_kernel grid %d x %d threads", D, uni ? "uniform" : "per-sequence", grid.x,
+                       grid.y, uni ? "splits x (sequence, KV head)" : "parts x KV head", a.B * a.Hq, D);
         if (uni)
             hipLaunchKernelGGL((decode_bf16_kernel<D, true>), grid, dim3(256), 0, st, a);
         else
@@ -549,6 +556,9 @@ hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
     } else {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hq))
                               : dim3((unsigned)a.n_parts, (unsigned)a.Hq);
+        if (log_enabled())
+            log_printf("  launch decode_f32_kernel<D=%d, %s> grid %u x %u x 64 threads, then decode_combine_kernel",
+                       D, uni ? "uniform" : "per-sequence", grid.x, grid.y);
         if (uni)
             hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
         else

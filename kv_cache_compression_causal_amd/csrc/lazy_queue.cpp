@@ -24,6 +24,11 @@
 
 extern "C" const char *lt_last_error(void);
 
+namespace lt {
+bool log_enabled();
+void log_printf(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+}  // namespace lt
+
 namespace {
 
 struct Entry {
@@ -151,6 +156,13 @@ int lt_lazy_queue_push(lt_lazy_queue *q, int layer, double score, int *evicted) 
     *evicted = q->step(Entry{score, layer});
     if (q->kv_set) q->kv.step(layer, *evicted, q->policy);
     q->next++;
+    if (lt::log_enabled()) {
+        if (q->kv_set)
+            lt::log_printf("lt_lazy_queue_push(layer=%d score=%.9g) -> evicted %d, KV retained %lld transient %lld",
+                           layer, score, *evicted, (long long)q->kv.retained, (long long)q->kv.transient);
+        else
+            lt::log_printf("lt_lazy_queue_push(layer=%d score=%.9g) -> evicted %d", layer, score, *evicted);
+    }
     return qfail(LT_OK, "");
 }
 

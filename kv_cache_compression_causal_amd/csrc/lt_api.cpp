@@ -4,6 +4,7 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "lt.h"
@@ -39,6 +40,15 @@ int hip_status(hipError_t e, const char *what) {
 void clear_stale_error() { (void)hipGetLastError(); }
 
 int elem_size(int dtype) { return dtype == LT_BF16 ? 2 : dtype == LT_F32 ? 4 : 0; }
+
+// A shape for the log (a thread-local buffer, valid until the next call).
+const char *shape_str(const lt_shape *s) {
+    thread_local char buf[128];
+    if (s == nullptr) return "shape=NULL";
+    snprintf(buf, sizeof(buf), "B=%d N=%d Hq=%d Hkv=%d D=%d dtype=%d scale=%g", s->B, s->N, s->Hq, s->Hkv, s->D,
+             s->dtype, (double)s->scale);
+    return buf;
+}
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -263,6 +273,44 @@ namespace lt_detail {
 void set_error(const char *msg) { snprintf(g_err, sizeof(g_err), "%s", msg); }
 }  // namespace lt_detail
 
+namespace lt {
+bool log_enabled() {
+    static const bool on = [] {
+        const char *e = getenv("LT_LOG");
+        return e != nullptr && e[0] != '\0' && strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+void log_printf(const char *fmt, ...) {
+    if (!log_enabled()) return;
+    char line[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(line, sizeof(line), fmt, ap);
+    va_end(ap);
+    fprintf(stderr, "[lt] %s\n", line);  // one write per line
+}
+}  // namespace lt
+
+namespace {
+// The outcome of a C-ABI call, when logging is on.
+int logged(int status, const char *call, const char *fmt, ...) __attribute__((format(printf, 3, 4)));
+int logged(int status, const char *call, const char *fmt, ...) {
+    if (!lt::log_enabled()) return status;
+    char args[320];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(args, sizeof(args), fmt, ap);
+    va_end(ap);
+    if (status == LT_OK)
+        lt::log_printf("%s(%s) -> LT_OK", call, args);
+    else
+        lt::log_printf("%s(%s) -> %s: %s", call, args, lt_status_str(status), g_err);
+    return status;
+}
+}  // namespace
+
 extern "C" {
 
 const char *lt_status_str(int status) {
@@ -284,32 +332,40 @@ const char *lt_last_error(void) { return g_err; }
 int lt_prefill_attn_lse_lazy(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
                              float *lse, int S, int R, int W, float *lazy_rows, float *lazy_ratio,
                              hipStream_t stream) {
-    return prefill(shape, nullptr, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream);
+    return logged(prefill(shape, nullptr, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream),
+                  "lt_prefill_attn_lse_lazy", "%s S=%d R=%d W=%d stream=%p", shape_str(shape), S, R, W, (void *)stream);
 }
 
 int lt_prefill_attn_lse_lazy_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
                                     lt_view v, lt_view out, float *lse, int S, int R, int W,
                                     float *lazy_rows, float *lazy_ratio, hipStream_t stream) {
-    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
-    return prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream);
+    const int rc = seq_lens == nullptr ? fail(LT_ERR_NULL, "seq_lens is NULL")
+                                       : prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio,
+                                                 stream);
+    return logged(rc, "lt_prefill_attn_lse_lazy_varlen", "%s S=%d R=%d W=%d stream=%p", shape_str(shape), S, R, W,
+                  (void *)stream);
 }
 
 int lt_prefill_attn_lse_lazy_emit(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k,
                                   lt_view v, lt_view out, float *lse, int S, int R, int W, float *lazy_rows,
                                   float *lazy_ratio, lt_view k_stream, lt_view v_stream, hipStream_t stream) {
-    return prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream, &k_stream,
-                   &v_stream);
+    return logged(prefill(shape, seq_lens, q, k, v, out, lse, S, R, W, lazy_rows, lazy_ratio, stream, &k_stream,
+                          &v_stream),
+                  "lt_prefill_attn_lse_lazy_emit", "%s S=%d R=%d W=%d lens=%s stream=%p", shape_str(shape), S, R, W,
+                  seq_lens ? "device" : "none", (void *)stream);
 }
 
 int lt_streaming_attn(const lt_shape *shape, lt_view q, lt_view k, lt_view v, lt_view out,
                       float *lse, int S, int R, hipStream_t stream) {
-    return streaming(shape, nullptr, q, k, v, out, lse, S, R, stream);
+    return logged(streaming(shape, nullptr, q, k, v, out, lse, S, R, stream), "lt_streaming_attn",
+                  "%s S=%d R=%d stream=%p", shape_str(shape), S, R, (void *)stream);
 }
 
 int lt_streaming_attn_varlen(const lt_shape *shape, const int32_t *seq_lens, lt_view q, lt_view k, lt_view v,
                              lt_view out, float *lse, int S, int R, hipStream_t stream) {
-    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
-    return streaming(shape, seq_lens, q, k, v, out, lse, S, R, stream);
+    const int rc = seq_lens == nullptr ? fail(LT_ERR_NULL, "seq_lens is NULL")
+                                       : streaming(shape, seq_lens, q, k, v, out, lse, S, R, stream);
+    return logged(rc, "lt_streaming_attn_varlen", "%s S=%d R=%d stream=%p", shape_str(shape), S, R, (void *)stream);
 }
 
 int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_len, size_t *bytes) {
@@ -324,48 +380,64 @@ int lt_hybrid_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int64_t kv_l
 int lt_hybrid_decode_attn(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
                           lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
                           void *ws, size_t ws_bytes, hipStream_t stream) {
-    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, ws, ws_bytes,
-                  stream);
+    return logged(decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, ws, ws_bytes,
+                         stream),
+                  "lt_hybrid_decode_attn", "B=%d Hq=%d Hkv=%d D=%d dtype=%d kv_len=%lld ws_bytes=%zu stream=%p", B, Hq,
+                  Hkv, D, dtype, (long long)kv_len, ws_bytes, (void *)stream);
 }
 
 int lt_hybrid_decode_attn_noalloc(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
                                   lt_view k_cache, lt_view v_cache, int64_t kv_len, void *out, float *lse,
                                   hipStream_t stream) {
-    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, nullptr, 0, stream,
-                  true);
+    return logged(decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, kv_len, nullptr, out, lse, nullptr, 0,
+                         stream, true),
+                  "lt_hybrid_decode_attn_noalloc", "B=%d Hq=%d Hkv=%d D=%d dtype=%d kv_len=%lld stream=%p", B, Hq, Hkv,
+                  D, dtype, (long long)kv_len, (void *)stream);
 }
 
 int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
                                  lt_view k_cache, lt_view v_cache, const int32_t *kv_lens, int64_t max_kv_len,
                                  void *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (kv_lens == nullptr) return fail(LT_ERR_NULL, "kv_lens is NULL");
-    return decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, max_kv_len, kv_lens, out, lse, ws,
-                  ws_bytes, stream);
+    const int rc = kv_lens == nullptr ? fail(LT_ERR_NULL, "kv_lens is NULL")
+                                      : decode(B, Hq, Hkv, D, dtype, scale, q, k_cache, v_cache, max_kv_len, kv_lens,
+                                               out, lse, ws, ws_bytes, stream);
+    return logged(rc, "lt_hybrid_decode_attn_varlen",
+                  "B=%d Hq=%d Hkv=%d D=%d dtype=%d max_kv_len=%lld ws_bytes=%zu stream=%p", B, Hq, Hkv, D, dtype,
+                  (long long)max_kv_len, ws_bytes, (void *)stream);
 }
 
 int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, int B,
                             int Hkv, int N, int D, int dtype, int S, int R, hipStream_t stream) {
-    return compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R, nullptr, stream);
+    return logged(compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R, nullptr, stream),
+                  "lt_compact_kv_streaming", "B=%d Hkv=%d N=%d D=%d dtype=%d S=%d R=%d stream=%p", B, Hkv, N, D,
+                  dtype, S, R, (void *)stream);
 }
 
 int lt_compact_kv_streaming_varlen(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream,
                                    int B, int Hkv, int N, int D, int dtype, int S, int R,
                                    const int32_t *seq_lens, hipStream_t stream) {
-    if (seq_lens == nullptr) return fail(LT_ERR_NULL, "seq_lens is NULL");
-    return compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R, seq_lens, stream);
+    const int rc = seq_lens == nullptr ? fail(LT_ERR_NULL, "seq_lens is NULL")
+                                       : compact(k_full, v_full, k_stream, v_stream, B, Hkv, N, D, dtype, S, R,
+                                                 seq_lens, stream);
+    return logged(rc, "lt_compact_kv_streaming_varlen", "B=%d Hkv=%d N=%d D=%d dtype=%d S=%d R=%d stream=%p", B,
+                  Hkv, N, D, dtype, S, R, (void *)stream);
 }
 
 int lt_stream_cache_append(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
                            int B, int Hkv, int D, int dtype, int S, int R, int64_t pos,
                            hipStream_t stream) {
-    return append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, pos, nullptr, stream);
+    return logged(append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, pos, nullptr, stream),
+                  "lt_stream_cache_append", "B=%d Hkv=%d D=%d dtype=%d S=%d R=%d pos=%lld stream=%p", B, Hkv, D,
+                  dtype, S, R, (long long)pos, (void *)stream);
 }
 
 int lt_stream_cache_append_varlen(lt_view k_stream, lt_view v_stream, const void *k_new, const void *v_new,
                                   int B, int Hkv, int D, int dtype, int S, int R, const int32_t *pos,
                                   hipStream_t stream) {
-    if (pos == nullptr) return fail(LT_ERR_NULL, "pos is NULL");
-    return append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, 0, pos, stream);
+    const int rc = pos == nullptr ? fail(LT_ERR_NULL, "pos is NULL")
+                                  : append(k_stream, v_stream, k_new, v_new, B, Hkv, D, dtype, S, R, 0, pos, stream);
+    return logged(rc, "lt_stream_cache_append_varlen", "B=%d Hkv=%d D=%d dtype=%d S=%d R=%d stream=%p", B, Hkv, D,
+                  dtype, S, R, (void *)stream);
 }
 
 int lt_kv_bytes(int B, int Hkv, int64_t N, int D, int dtype, int S, int R, int64_t *full_bytes,

@@ -8,6 +8,12 @@
 
 namespace lt {
 
+// Library-side logging: with the environment variable LT_LOG set (to
+// anything but "0"), every C-ABI call prints one line to stderr (call,
+// sizes, status) and every kernel launch its kernel and launch shape.
+bool log_enabled();
+void log_printf(const char *fmt, ...) __attribute__((format(printf, 1, 2)));
+
 typedef __bf16 bf16;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
@@ -114,6 +120,21 @@ __device__ __forceinline__ void emit_stream_rows(const char *kbase, const char *
             : (char *)so.v + ((int64_t)b * so.vs_sb + (int64_t)hk * so.vs_sh + slot * so.vs_sn) * elem;
         *(uint4 *)(dst + ch * 16) = *(const uint4 *)(src + ch * 16);
     }
+}
+
+// Debug builds (compiled with LT_POISON_LDS, liblt_debug.so): a kernel fills
+// its LDS with all-ones words -- NaN as bf16 and as fp32 -- before first use,
+// so that a read of LDS the kernel never wrote shows up in its outputs; the
+// debug library's results must equal the release library's bit for bit.
+// NT threads of the workgroup take part; bytes is a multiple of 16.
+template <int NT>
+__device__ __forceinline__ void poison_lds(void *lds, int bytes, int tid) {
+#ifdef LT_POISON_LDS
+    for (int i = tid * 16; i < bytes; i += NT * 16) *(uint4 *)((char *)lds + i) = make_uint4(~0u, ~0u, ~0u, ~0u);
+    __syncthreads();
+#else
+    (void)lds, (void)bytes, (void)tid;
+#endif
 }
 
 // Length of sequence b: N, or seq_len[b] clamped to [0, N].

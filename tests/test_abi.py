@@ -455,3 +455,31 @@ def test_binding_refuses_host_tensors_and_bad_lazy_buffers():
     with pytest.raises(ValueError, match="on the GPU"):
         api.lt_compact_kv_streaming(k, k, torch.zeros(B, Hkv, 12, D, dtype=torch.bfloat16),
                                     torch.zeros(B, Hkv, 12, D, dtype=torch.bfloat16), 4, 8)
+
+
+def test_lt_log_prints_calls_and_their_status():
+    """With LT_LOG=1 every C-ABI call prints one line on stderr (call, sizes,
+    status and message), queue pushes their decision and KV bytes; without
+    it nothing is printed.  Host-only calls here: nothing is launched."""
+    import subprocess
+    import sys
+    code = (
+        "import ctypes\n"
+        "from kv_cache_compression_causal_amd import _lib, api\n"
+        "L = _lib.lib()\n"
+        "shp = _lib.LtShape(1, 64, 4, 2, 96, _lib.LT_BF16, 0.0)\n"
+        "v = _lib.LtView(0x100000, 1 << 20, 1 << 16, 128)\n"
+        "print(L.lt_prefill_attn_lse_lazy(ctypes.byref(shp), v, v, v, v, 0x100000, 4, 8, 4, 0x100000, 0x100000, None))\n"
+        "q = api.LazyQueue(3, 1)\n"
+        "q.set_kv_bytes(100, 10)\n"
+        "print(q.push(0, 0.5), q.push(1, 0.25))\n"
+    )
+    env = dict(os.environ, LT_LOG="1")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [ln for ln in r.stderr.splitlines() if ln.startswith("[lt] ")]
+    assert any("lt_prefill_attn_lse_lazy(" in ln and "LT_ERR_DTYPE" in ln and "D=96" in ln for ln in lines), lines
+    assert any("lt_lazy_queue_push(layer=1" in ln and "evicted 0" in ln and "retained 110 transient 200" in ln for ln in lines), lines
+    env["LT_LOG"] = "0"
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "[lt] " not in r.stderr

@@ -323,3 +323,66 @@ def test_permuted_views_match_contiguous(dtype):
     for b, n in enumerate(lens):
         assert torch.equal(vout_p[b, :, :n], vref[0][b, :, :n]) and torch.equal(vlse[b, :, :n], vref[1][b, :, :n])
     assert torch.equal(vratio, vref[3]) and torch.equal(kvout, kvref[0]) and torch.equal(kvlse, kvref[1])
+
+
+def test_debug_build_with_poisoned_lds_gives_the_same_bits():
+    """liblt_debug.so (every kernel fills its LDS with NaN before first use)
+    against liblt.so on the same inputs: identical bits for prefill + lazy
+    (both workgroup shapes), fp32, streaming, the emitted slice and decode
+    (uniform and per-sequence contexts), so no kernel reads LDS it did not
+    write."""
+    import contextlib
+    from kv_cache_compression_causal_amd import _lib
+    debug = _lib.load_library(_lib.DEBUG_LIB_PATH)
+    release = _lib.lib()
+
+    @contextlib.contextmanager
+    def using(library):
+        saved = _lib._lib
+        _lib._lib = library
+        try:
+            yield
+        finally:
+            _lib._lib = saved
+
+    def run():
+        res = []
+        for (B, N, Hq, Hkv, D, dtype, S, R, W, seed) in [(2, 300, 10, 2, 128, torch.bfloat16, 4, 100, 40, 41),
+                                                         (1, 6140, 64, 8, 128, torch.bfloat16, 4, 300, 48, 42),
+                                                         (1, 257, 4, 2, 64, torch.bfloat16, 4, 33, 16, 43),
+                                                         (1, 300, 8, 2, 128, torch.float32, 4, 60, 50, 44)]:
+            q, k, v = synth.qkv(B, N, Hq, Hkv, D, seed, dtype, device=DEV)
+            res += list(ops.prefill(q, k, v, S, R, W)) + list(ops.streaming(q, k, v, S, R))
+            res += list(ops.prefill_emit(q, k, v, S, R, W))
+            qd = q[:, :, -1].contiguous()
+            res += list(ops.decode(qd, k, v)) + list(ops.decode_varlen(qd, k, v, [N - 7 * b for b in range(B)]))
+        torch.cuda.synchronize()
+        return res
+
+    print("release vs debug (LDS poisoned) library", flush=True)
+    with using(release):
+        want = run()
+    with using(debug):
+        got = run()
+    assert len(got) == len(want)
+    for i, (g_, w_) in enumerate(zip(got, want)):
+        assert torch.equal(g_.view(torch.uint8), w_.view(torch.uint8)), f"output {i} differs"
+
+
+def test_lt_log_prints_each_launch():
+    """LT_LOG=1 on the GPU: the call line and the launch line naming the
+    kernel and its grid (a child process, so the setting stays local)."""
+    import os
+    import subprocess
+    import sys
+    code = ("import torch\n"
+            "from kv_cache_compression_causal_amd import ops, synth\n"
+            "q, k, v = synth.qkv(1, 200, 8, 2, 128, 5, torch.bfloat16, device='cuda')\n"
+            "ops.prefill(q, k, v, 4, 60, 32)\n"
+            "torch.cuda.synchronize()\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, env=dict(os.environ, LT_LOG="1"),
+                       capture_output=True, text=True, timeout=150)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert "lt_prefill_attn_lse_lazy(B=1 N=200 Hq=8 Hkv=2 D=128" in r.stderr and "-> LT_OK" in r.stderr
+    assert "launch attn_bf16_kernel<D=128" in r.stderr and "launch lazy_reduce_kernel" in r.stderr
