@@ -391,9 +391,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     // One key tile: prefetch the next tile into the other buffer, then the
     // tile's 32-key steps.  BUF is a compile-time constant so that every LDS
-    // address of the steps is a fixed offset.
-    auto run_tile = [&](int it, auto buf_c) {
+    // address of the steps is a fixed offset; FIRST marks the wave's first
+    // tile, whose first step streaming attention runs without the lagging
+    // max.
+    auto run_tile = [&](int it, auto buf_c, auto first_c) {
         constexpr int BUF = decltype(buf_c)::value;
+        constexpr bool FIRST = decltype(first_c)::value;
         bf16 *const Kb = lds + BUF * TILE;
         bf16 *const Vb = lds + (2 + BUF) * TILE;
         if (it + 1 < n_iter) load_tile(tile_of(it + 1), lds + (BUF ^ 1) * TILE, lds + (2 + (BUF ^ 1)) * TILE);
@@ -446,6 +449,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                         rs[rb] = e == 0 ? p0 + p1 : rs[rb] + (p0 + p1);
                     }
             };
+            if (MODE == MODE_STREAM && FIRST && h == 0) {
+                // The wave's first step: O, l and lz are still zero, so the
+                // exact row max is taken at once and nothing is rescaled (the
+                // general path would reach the same values after a rescale
+                // by exp2(kMInit - max) = 0).
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    float mx = kNegInf;
+#pragma unroll
+                    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][rb][r]);
+                    m[rb] = fmaxf(m[rb], group_max(mx) * c);
+                }
+                weights();
+            } else {
             weights();
             bool outgrown = false;
 #pragma unroll
@@ -471,6 +490,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     for (int db = 0; db < DB; ++db) o[rb][db] *= alpha;
                 }
                 weights();
+            }
             }
             if (!INPLACE) {
 #pragma unroll
@@ -512,12 +532,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
     load_tile(tile_of(0), lds, lds + 2 * TILE);
     loads_done();
-    int it = 0;
-    for (; it + 1 < n_iter; it += 2) {
-        run_tile(it, std::integral_constant<int, 0>{});
-        run_tile(it + 1, std::integral_constant<int, 1>{});
+    if (MODE == MODE_STREAM) {
+        // n_iter >= 1: the band holds at least the tile of the last row.
+        run_tile(0, std::integral_constant<int, 0>{}, std::true_type{});
+        int it = 1;
+        for (; it + 1 < n_iter; it += 2) {
+            run_tile(it, std::integral_constant<int, 1>{}, std::false_type{});
+            run_tile(it + 1, std::integral_constant<int, 0>{}, std::false_type{});
+        }
+        if (it < n_iter) run_tile(it, std::integral_constant<int, 1>{}, std::false_type{});
+    } else {
+        int it = 0;
+        for (; it + 1 < n_iter; it += 2) {
+            run_tile(it, std::integral_constant<int, 0>{}, std::false_type{});
+            run_tile(it + 1, std::integral_constant<int, 1>{}, std::false_type{});
+        }
+        if (it < n_iter) run_tile(it, std::integral_constant<int, 0>{}, std::false_type{});
     }
-    if (it < n_iter) run_tile(it, std::integral_constant<int, 0>{});
 
     // Finalize: O / l, LSE = (m + log2 l) * ln 2, lazy row = lz / l.
     // Streaming goes through the (now idle) LDS tile buffers: each wave
