@@ -174,6 +174,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr int NI = (NINST + NW - 1) / NW;
     constexpr int TILE = BT * D;
     static_assert(BT % RPI == 0, "tile rows must fill whole direct loads");
+    static_assert(MODE != MODE_STREAM || NW * 16 * RB * D <= 4 * TILE,
+                  "streaming stages every wave's output rows in the tile buffers");
     constexpr bool LAZY = MODE == MODE_FULL_LAZY;
     __shared__ __attribute__((aligned(16))) bf16 lds[4 * TILE];  // K0 K1 V0 V1
 
