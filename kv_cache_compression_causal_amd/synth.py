@@ -29,7 +29,7 @@ contexts up to 100K tokens; real prompts and weights are not used):
 from __future__ import annotations
 
 from dataclasses import dataclass, field
-from typing import Dict, Optional, Tuple
+from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 import torch
@@ -86,17 +86,23 @@ def normal(shape, seed: int, dtype=torch.float32, device="cpu",
 
 
 def qkv(B: int, N: int, Hq: int, Hkv: int, D: int, seed: int, dtype=torch.bfloat16,
-        device="cpu", sink_tokens: int = 0, sink_scale: float = 1.0
+        device="cpu", sink_tokens: int = 0, sink_scale: float = 1.0,
+        spikes: Sequence[Tuple[int, float]] = ()
         ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
     """q [B,Hq,N,D], k/v [B,Hkv,N,D] ~ N(0,1) from one seeded generator.
     Keys of the first ``sink_tokens`` positions are multiplied by
-    ``sink_scale`` in fp32 before rounding."""
+    ``sink_scale`` in fp32 before rounding, and the key at each position p of
+    ``spikes`` by its factor (scores against it then reach many times the
+    spread of the others, in both signs)."""
     g = _gen(seed, device)
     q = torch.randn(B, Hq, N, D, generator=g, device=device, dtype=torch.float32)
     k = torch.randn(B, Hkv, N, D, generator=g, device=device, dtype=torch.float32)
     v = torch.randn(B, Hkv, N, D, generator=g, device=device, dtype=torch.float32)
     if sink_tokens > 0 and sink_scale != 1.0:
         k[:, :, :sink_tokens, :] *= sink_scale
+    for p, f in spikes:
+        if 0 <= p < N:
+            k[:, :, p, :] *= f
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
