@@ -36,6 +36,8 @@ PREFILL_CASES = [
     (1, 40, 5, 1, 128, torch.bfloat16, 8, 64, 10, 19),    # S+R >= N
     (1, 300, 8, 2, 128, torch.float32, 4, 60, 50, 20),    # fp32 D=128 G=4
     (2, 130, 6, 3, 64, torch.float32, 0, 7, 130, 21),     # fp32 W=N S=0
+    (1, 150, 32, 2, 128, torch.bfloat16, 4, 40, 30, 22),  # G=16
+    (1, 97, 16, 1, 64, torch.bfloat16, 4, 20, 9, 23),     # G=16, D=64
 ]
 
 
@@ -105,6 +107,7 @@ STREAM_CASES = [
     (1, 700, 16, 2, 128, torch.bfloat16, 5, 250, 9),   # G=8
     (1, 640, 4, 2, 64, torch.bfloat16, 33, 150, 10),   # a step of sinks only, then a mixed one
     (1, 800, 5, 1, 128, torch.bfloat16, 64, 128, 11),  # two whole sink steps
+    (1, 300, 32, 2, 128, torch.bfloat16, 4, 60, 12),   # G=16
 ]
 
 
