@@ -84,15 +84,16 @@ def median(xs):
     return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
 
 
-def traffic_from_profile(src_path: str, prof_path: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None
-    if the summary is missing or the kernel source changed since."""
+def traffic_from_profile(src_path: str, prof_path: str, key: str = "hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per step, with key) from a committed
+    rocprofv3 --pmc summary, or None if the summary is missing or the kernel
+    source changed since."""
     if not os.path.exists(prof_path):
         return None
     text = open(prof_path).read()
     sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
     m_sha = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
-    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_b = re.search(key + r":\s*([0-9.eE+]+)", text)
     if not m_sha or not m_b or m_sha.group(1) != sha:
         return None
     return float(m_b.group(1))
@@ -809,9 +810,13 @@ def main() -> int:
                                                                   "(a replayed HIP graph), median of replays",
                                       "global_batch": 8, "seq_len": 100000, "parallelism": "none (1 GPU)",
                                       **({"overrides": overrides} if overrides else {})}})
+            traffic = traffic_from_profile(os.path.join(ROOT, "kv_cache_compression_causal_amd", "csrc", "decode.hip"),
+                                           os.path.join(ROOT, "profiles", "decode100k_pmc.txt"), "hbm_bytes_per_step")
             result["roofline"] = {"bound": "hbm", "achieved": d["gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                                  "frac": d["frac_hbm_peak"], "traffic": None,
-                                  "kernel": "decode_bf16_kernel<D=128> + decode_combine_kernel (64 layers)"}
+                                  "frac": d["frac_hbm_peak"], "traffic": traffic,
+                                  "kernel": "decode_bf16_kernel<D=128> + decode_combine_kernel (64 layers)",
+                                  "what": "algorithmic bytes per step / median step time of the replayed graph; "
+                                          "traffic: FETCH_SIZE + WRITE_SIZE bytes of one step"}
             if not args.no_cpu:
                 result["cpu_baseline"] = bench.cpu_decode()
         elif not args.no_cpu and "cpu_baseline" in result:
