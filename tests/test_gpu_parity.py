@@ -389,3 +389,65 @@ def test_lt_log_prints_each_launch():
     assert r.returncode == 0, r.stderr[-2000:]
     assert "lt_prefill_attn_lse_lazy(B=1 N=200 Hq=8 Hkv=2 D=128" in r.stderr and "-> LT_OK" in r.stderr
     assert "launch attn_bf16_kernel<D=128" in r.stderr and "launch lazy_reduce_kernel" in r.stderr
+
+
+def test_layer_calls_captured_in_a_graph():
+    """Prefill + lazy ratio, streaming, compaction and decode of one layer
+    captured in one HIP graph on a side stream, replayed three times after
+    new inputs were copied in eagerly (with unrelated eager work and a
+    synchronisation between replays): every replay gives the eager calls'
+    bits on the same inputs.  The library issues no memset or allocation,
+    so nothing in the graph depends on capture-time state."""
+    from kv_cache_compression_causal_amd import api
+    B, N, Hq, Hkv, D, S, R, W = 1, 700, 8, 2, 128, 4, 100, 40
+    G = Hq // Hkv
+    q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, 61, torch.bfloat16))
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, N, device=DEV, dtype=torch.float32)
+    rows = torch.empty(B, Hq, W, device=DEV, dtype=torch.float32)
+    ratio = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    sout = torch.empty_like(q)
+    slse = torch.empty(B, Hq, N, device=DEV, dtype=torch.float32)
+    ks = torch.empty(B, Hkv, S + R, D, device=DEV, dtype=torch.bfloat16)
+    vs = torch.empty_like(ks)
+    qt = torch.empty(B, Hq, D, device=DEV, dtype=torch.bfloat16)
+    dout = torch.empty_like(qt)
+    dlse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    ws = ops.decode_workspace(B, Hq, Hkv, D, S + R, DEV)
+    outs = (out, lse, rows, ratio, sout, slse, ks, vs, dout, dlse)
+
+    def layer(st):
+        api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, st)
+        api.lt_streaming_attn(q, k, v, sout, slse, S, R, 0.0, st)
+        api.lt_compact_kv_streaming(k, v, ks, vs, S, R, st)
+        qt.copy_(q[:, :, -1])
+        api.lt_hybrid_decode_attn(qt, ks, vs, S + R, dout, dlse, ws, 0.0, st)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        layer(s)                                              # warm call
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=s):
+        layer(s)
+    torch.cuda.synchronize()
+    for seed in (62, 63, 64):
+        print(f"graph replay, inputs seed {seed}", flush=True)
+        nq, nk, nv = synth.qkv(B, N, Hq, Hkv, D, seed, torch.bfloat16)
+        q.copy_(nq), k.copy_(nk), v.copy_(nv)
+        _ = (q.float() * 2.0).sum()                           # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in outs]
+        with torch.cuda.stream(s):
+            layer(s)                                          # eager, same inputs
+        torch.cuda.synchronize()
+        for i, (g_, w_) in enumerate(zip(got, outs)):
+            assert torch.equal(g_.view(torch.uint8), w_.view(torch.uint8)), f"replay (seed {seed}) output {i} differs"
+    # and the eager results are right
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, W=W, streaming=True)
+    assert_close("out", np64(out), ref["out"], TOL_BF16_OUT)
+    assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], TOL_BF16_RATIO)
+    assert_close("sout", np64(sout), ref["sout"], TOL_BF16_OUT)
