@@ -1,0 +1,90 @@
+"""GPU parity on seeded random shapes, beside the hand-picked cases: batch,
+length (1 to 1200, log-uniform), GQA group (1-8 and 16), KV heads, head
+dimension, dtype, sinks, window and observed rows drawn from one seeded
+generator.  Each case runs prefill + lazy ratio, streaming attention, the
+per-sequence-length prefill at random lengths, and decode of the last row
+over the full cache, all against the fp64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from kv_cache_compression_causal_amd import ops, synth
+from helpers import (TOL_BF16_LSE, TOL_BF16_OUT, TOL_BF16_RATIO, TOL_F32, assert_close, np64)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _cases(n=100, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
+        Hkv = int(rng.choice([1, 2, 3, 4, 8]))
+        G = int(rng.choice([1, 2, 3, 4, 5, 6, 8, 16]))
+        B = int(rng.choice([1, 1, 2, 3]))
+        N = int(np.clip(np.exp(rng.uniform(0, np.log(1200))), 1, 1200))
+        while B * Hkv * G * N > 120_000:   # keep the oracle at a second or two
+            N = max(1, N // 2)
+        S = int(rng.choice([0, 1, 4, 33, 64]))
+        R = int(rng.integers(1, 401))
+        W = int(rng.integers(1, N + 1))
+        out.append((B, N, G * Hkv, Hkv, D, dtype, S, R, W, 300 + i))
+    return out
+
+
+CASES = _cases()
+
+
+def _tol(dtype):
+    if dtype == torch.float32:
+        return TOL_F32, TOL_F32, TOL_F32
+    return TOL_BF16_OUT, TOL_BF16_LSE, TOL_BF16_RATIO
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,dtype,S,R,W,seed", CASES,
+                         ids=[f"B{c[0]}-N{c[1]}-Hq{c[2]}-Hkv{c[3]}-D{c[4]}-{'f32' if c[5] == torch.float32 else 'bf16'}"
+                              f"-S{c[6]}-R{c[7]}-W{c[8]}" for c in CASES])
+def test_random_shape(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
+    print(f"random shape B{B} N{N} Hq{Hq} Hkv{Hkv} D{D} {dtype} S{S} R{R} W{W} seed {seed}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, seed, dtype)
+    to, tl, tr = _tol(dtype)
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, W=W, streaming=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, rows, ratio = ops.prefill(qd, kd, vd, S, R, W)
+    sout, slse = ops.streaming(qd, kd, vd, S, R)
+    dq = qd[:, :, -1].contiguous()
+    dout, dlse = ops.decode(dq, kd, vd)
+    torch.cuda.synchronize()
+    assert_close("out", np64(out), ref["out"], to)
+    assert_close("lse", np64(lse), ref["lse"], tl)
+    assert_close("lazy_rows", np64(rows), ref["lazy_rows"], tr)
+    assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], tr)
+    assert_close("sout", np64(sout), ref["sout"], to)
+    assert_close("slse", np64(slse), ref["slse"], tl)
+    # decode of the last query over the whole cache is prefill's last row
+    assert_close("decode out", np64(dout), ref["out"][:, :, -1], to)
+    assert_close("decode lse", np64(dlse), ref["lse"][:, :, -1], tl)
+    # per-sequence lengths: random lengths in [0, N], the padded rows hold large values
+    rng = np.random.default_rng(seed)
+    lens = [int(x) for x in rng.integers(0, N + 1, size=B)]
+    lens[0] = N
+    kp, vp = k.clone(), v.clone()
+    for b, n in enumerate(lens):
+        kp[b, :, n:] = 30.0
+        vp[b, :, n:] = -200.0
+    rv = oracle.prefill_varlen(np64(q), np64(kp), np64(vp), lens, S=S, R=R, W=W, streaming=False)
+    vo, vl, vr, vrat = ops.prefill_varlen(qd, kp.to(DEV), vp.to(DEV), lens, S, R, W)
+    torch.cuda.synchronize()
+    got_rows = np64(vr)
+    for b, n in enumerate(lens):
+        if n == 0:
+            continue
+        assert_close(f"varlen out b{b}", np64(vo[b, :, :n]), rv["out"][b, :, :n], to)
+        assert_close(f"varlen lse b{b}", np64(vl[b, :, :n]), rv["lse"][b, :, :n], tl)
+        w = min(W, n)
+        assert_close(f"varlen lazy rows b{b}", got_rows[b, :, W - w:], rv["lazy_rows"][b, :, W - w:], tr)
+        assert_close(f"varlen ratio b{b}", np64(vrat[b]), rv["lazy_ratio"][b], tr)
