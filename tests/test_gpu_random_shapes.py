@@ -88,3 +88,52 @@ def test_random_shape(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
         w = min(W, n)
         assert_close(f"varlen lazy rows b{b}", got_rows[b, :, W - w:], rv["lazy_rows"][b, :, W - w:], tr)
         assert_close(f"varlen ratio b{b}", np64(vrat[b]), rv["lazy_ratio"][b], tr)
+
+
+def _large_cases(n=6, seed=77):
+    """Grids of at least four 8-wave workgroups per CU (the 128-key shape)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        D = int(rng.choice([64, 128]))
+        Hkv = int(rng.choice([4, 8]))
+        G = int(rng.choice([2, 4, 5, 8]))
+        B = int(rng.choice([1, 2]))
+        rows_needed = 1024 * 384 // (B * Hkv)          # flattened rows per (b, KV head)
+        N = int(rng.integers(rows_needed // G + 1, rows_needed // G + 3000))
+        S = int(rng.choice([0, 4, 33]))
+        R = int(rng.integers(16, 1100))
+        W = int(rng.integers(1, 129))
+        out.append((B, N, G * Hkv, Hkv, D, S, R, W, 400 + i))
+    return out
+
+
+LARGE = _large_cases()
+
+
+@pytest.mark.parametrize("B,N,Hq,Hkv,D,S,R,W,seed", LARGE,
+                         ids=[f"B{c[0]}-N{c[1]}-Hq{c[2]}-Hkv{c[3]}-D{c[4]}-S{c[5]}-R{c[6]}-W{c[7]}" for c in LARGE])
+def test_random_large_grid_shape(B, N, Hq, Hkv, D, S, R, W, seed):
+    """bf16, the 8-wave kernel: sampled rows of every (batch, head) -- the first
+    rows, the last W, the ragged end and random ones -- for prefill + lazy
+    ratio and streaming."""
+    assert (N * (Hq // Hkv) + 383) // 384 * B * Hkv >= 1024
+    print(f"random large grid B{B} N{N} Hq{Hq} Hkv{Hkv} D{D} S{S} R{R} W{W} seed {seed}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, seed, torch.bfloat16, device=DEV)
+    out, lse, rows, ratio = ops.prefill(q, k, v, S, R, W)
+    sout, slse = ops.streaming(q, k, v, S, R)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    rng = np.random.default_rng(seed)
+    for b in range(B):
+        for h in range(Hq):
+            pos = np.unique(np.concatenate([np.arange(0, 4), np.arange(N - W, N), rng.integers(0, N, 6)])).astype(np.int32)
+            pt = torch.as_tensor(pos, device=DEV, dtype=torch.long)
+            r = oracle.rows(np64(k[b, h // G]), np64(v[b, h // G]), pos, np64(q[b, h][pt]), S=S, R=R)
+            assert_close(f"out b{b} h{h}", np64(out[b, h][pt]), r["out"], TOL_BF16_OUT)
+            assert_close(f"lse b{b} h{h}", np64(lse[b, h][pt]), r["lse"], TOL_BF16_LSE)
+            assert_close(f"stream out b{b} h{h}", np64(sout[b, h][pt]), r["sout"], TOL_BF16_OUT)
+            assert_close(f"stream lse b{b} h{h}", np64(slse[b, h][pt]), r["slse"], TOL_BF16_LSE)
+            obs = pos >= N - W
+            assert_close(f"lazy rows b{b} h{h}", np64(rows[b, h]), r["lazy"][obs], TOL_BF16_RATIO)
+            assert abs(float(ratio[b, h]) - r["lazy"][obs].mean()) <= TOL_BF16_RATIO
