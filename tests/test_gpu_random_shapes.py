@@ -3,13 +3,14 @@ length (1 to 1200, log-uniform), GQA group (1-8 and 16), KV heads, head
 dimension, dtype, sinks, window and observed rows drawn from one seeded
 generator.  Each case runs prefill + lazy ratio, streaming attention, the
 per-sequence-length prefill at random lengths, and decode of the last row
-over the full cache, all against the fp64 oracle."""
+over the full cache, all against the fp64 oracle, and the streaming slice
+(compaction, and the prefill that writes it) bit for bit."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from kv_cache_compression_causal_amd import ops, synth
+from kv_cache_compression_causal_amd import api, ops, synth
 from helpers import (TOL_BF16_LSE, TOL_BF16_OUT, TOL_BF16_RATIO, TOL_F32, assert_close, np64)
 
 pytestmark = pytest.mark.gpu
@@ -68,6 +69,18 @@ def test_random_shape(B, N, Hq, Hkv, D, dtype, S, R, W, seed):
     # decode of the last query over the whole cache is prefill's last row
     assert_close("decode out", np64(dout), ref["out"][:, :, -1], to)
     assert_close("decode lse", np64(dlse), ref["lse"][:, :, -1], tl)
+    # the streaming slice: compaction, and the prefill writing it, bit for bit
+    keep = oracle.streaming_rows(N, S, R)
+    ks, vs = ops.compact(kd, vd, S, R)
+    ks2 = torch.full((B, Hkv, S + R, D), 7.0, device=DEV, dtype=dtype)
+    vs2 = torch.full_like(ks2, 7.0)
+    o2, l2 = torch.empty_like(qd), torch.empty_like(lse)
+    r2, t2 = torch.empty_like(rows), torch.empty_like(ratio)
+    api.lt_prefill_attn_lse_lazy_emit(qd, kd, vd, o2, l2, S, R, W, r2, t2, ks2, vs2, None)
+    torch.cuda.synchronize()
+    assert torch.equal(ks.cpu(), k[:, :, keep]) and torch.equal(vs.cpu(), v[:, :, keep])
+    assert torch.equal(ks2[:, :, :len(keep)].cpu(), k[:, :, keep]) and torch.equal(vs2[:, :, :len(keep)].cpu(), v[:, :, keep])
+    assert torch.equal(o2, out) and torch.equal(l2, lse) and torch.equal(r2, rows) and torch.equal(t2, ratio)
     # per-sequence lengths: random lengths in [0, N], the padded rows hold large values
     rng = np.random.default_rng(seed)
     lens = [int(x) for x in rng.integers(0, N + 1, size=B)]
