@@ -148,10 +148,13 @@ class Bench:
         1 ms matrix-core run stays below the clock a 10 ms one holds): run fn
         untimed for about `seconds` before a leg's own warm-up."""
         t_end = time.perf_counter() + seconds
+        n = 0
         while time.perf_counter() < t_end:
             for _ in range(8):
                 fn()
+            n += 8
             self.torch.cuda.synchronize()
+        return n
 
     def time_each(self, fn, reps, warm=None):
         """Durations (ms) of `reps` launches of fn, each bracketed by its own
@@ -247,13 +250,13 @@ class Bench:
                 finish(pending[0])
                 pending[0] = None
 
-        self.warm_clock(lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio_d[0], 0.0,
-                                                              stream))
+        n_warm = self.warm_clock(lambda: api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows,
+                                                                       ratio_d[0], 0.0, stream))
         for i in range(Wm):
             step(i)
         drain()
         torch.cuda.synchronize()
-        log(f"{w.name}: timing {K} steps")
+        log(f"{w.name}: timing {K} steps after {n_warm + Wm} untimed prefill launches")
         t0 = time.perf_counter()
         for i in range(K):
             step(i, i)
