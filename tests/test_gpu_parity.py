@@ -451,3 +451,49 @@ def test_layer_calls_captured_in_a_graph():
     assert_close("out", np64(out), ref["out"], TOL_BF16_OUT)
     assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], TOL_BF16_RATIO)
     assert_close("sout", np64(sout), ref["sout"], TOL_BF16_OUT)
+
+
+def test_calls_on_two_streams_at_once():
+    """Two layers' calls issued on two streams without synchronising in
+    between (prefill + lazy ratio, streaming, decode on each): the results
+    equal, bit for bit, those of the same calls run one after the other.  The
+    library keeps no state between calls (the allocation-free decode's array
+    aside, which these calls do not use)."""
+    from kv_cache_compression_causal_amd import api
+    B, N, Hq, Hkv, D, S, R, W = 1, 3000, 16, 4, 128, 4, 300, 40
+    sets = []
+    for seed in (71, 72):
+        q, k, v = (t.to(DEV) for t in synth.qkv(B, N, Hq, Hkv, D, seed, torch.bfloat16))
+        outs = dict(out=torch.empty_like(q), lse=torch.empty(B, Hq, N, device=DEV),
+                    rows=torch.empty(B, Hq, W, device=DEV), ratio=torch.empty(B, Hq, device=DEV),
+                    sout=torch.empty_like(q), slse=torch.empty(B, Hq, N, device=DEV),
+                    dout=torch.empty(B, Hq, D, device=DEV, dtype=torch.bfloat16),
+                    dlse=torch.empty(B, Hq, device=DEV),
+                    ws=ops.decode_workspace(B, Hq, Hkv, D, N, DEV), qt=q[:, :, -1].contiguous())
+        sets.append((q, k, v, outs))
+
+    def layer(q, k, v, o, st):
+        api.lt_prefill_attn_lse_lazy(q, k, v, o["out"], o["lse"], S, R, W, o["rows"], o["ratio"], 0.0, st)
+        api.lt_streaming_attn(q, k, v, o["sout"], o["slse"], S, R, 0.0, st)
+        api.lt_hybrid_decode_attn(o["qt"], k, v, N, o["dout"], o["dlse"], o["ws"], 0.0, st)
+
+    keys = ("out", "lse", "rows", "ratio", "sout", "slse", "dout", "dlse")
+    cur = torch.cuda.current_stream()
+    for q, k, v, o in sets:          # one after the other
+        layer(q, k, v, o, cur)
+        torch.cuda.synchronize()
+    want = [{kk: o[kk].clone() for kk in keys} for _, _, _, o in sets]
+    for _, _, _, o in sets:
+        for kk in keys:
+            o[kk].fill_(float("nan"))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for rep in range(3):
+        print(f"two streams, round {rep}", flush=True)
+        for (q, k, v, o), st in zip(sets, (s1, s2)):
+            st.wait_stream(cur)
+            layer(q, k, v, o, st)
+        torch.cuda.synchronize()
+        for i, (_, _, _, o) in enumerate(sets):
+            for kk in keys:
+                assert torch.equal(o[kk].view(torch.uint8), want[i][kk].view(torch.uint8)), f"set {i} {kk} differs"
