@@ -639,18 +639,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // Per-head lazy ratio: mean of the observed rows, summed in row order.  A
 // sequence observes its last min(W, n) rows; slot k holds row n - W + k, so
-// the slots of rows before position 0 (n < W) are set to NaN.
-__global__ void lazy_reduce_kernel(float *rows, float *ratio, int BH, int W, const int *seq_len, int Hq,
-                                   int N) {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+// the slots of rows before position 0 (n < W) are set to NaN.  One wave per
+// (batch, head): the wave stages the rows in LDS, 16 per lane in one
+// coalesced round per chunk, and lane 0 adds them in row order.  (One thread
+// per head reading its rows from memory one after the other took about
+// 12 us for W = 128, a few per cent of an 8K-token layer.)
+constexpr int kReduceChunk = 1024;
+__global__ __launch_bounds__(64) void lazy_reduce_kernel(float *rows, float *ratio, int BH, int W,
+                                                         const int *seq_len, int Hq, int N) {
+    __shared__ float sh[kReduceChunk];
+    const int i = blockIdx.x, lane = threadIdx.x;
     if (i >= BH) return;
+    poison_lds<64>(sh, (int)sizeof(sh), lane);
     const int n = seq_length(seq_len, i / Hq, N);
     const int cnt = n < W ? n : W;
     float *r = rows + (int64_t)i * W;
-    for (int w = 0; w < W - cnt; ++w) r[w] = __builtin_nanf("");
+    for (int w = lane; w < W - cnt; w += 64) r[w] = __builtin_nanf("");
     float acc = 0.f;
-    for (int w = W - cnt; w < W; ++w) acc += r[w];
-    ratio[i] = cnt > 0 ? acc / (float)cnt : __builtin_nanf("");
+    for (int c0 = W - cnt; c0 < W; c0 += kReduceChunk) {
+        const int len = W - c0 < kReduceChunk ? W - c0 : kReduceChunk;
+        for (int w = lane; w < len; w += 64) sh[w] = r[c0 + w];
+        __syncthreads();
+        if (lane == 0)
+            for (int w = 0; w < len; ++w) acc += sh[w];
+        __syncthreads();
+    }
+    if (lane == 0) ratio[i] = cnt > 0 ? acc / (float)cnt : __builtin_nanf("");
 }
 
 // MODES: bit mask of the modes this configuration is built for.
@@ -728,9 +742,9 @@ hipError_t launch_attn_bf16(const AttnArgs &a, int D, int mode, hipStream_t st) 
 
 hipError_t launch_lazy_reduce(float *lazy_rows, float *lazy_ratio, int BH, int W, const int *seq_len,
                               int Hq, int N, hipStream_t st) {
-    if (log_enabled()) log_printf("  launch lazy_reduce_kernel grid %d x 256 threads", (BH + 255) / 256);
-    hipLaunchKernelGGL(lazy_reduce_kernel, dim3((BH + 255) / 256), dim3(256), 0, st, lazy_rows,
-                       lazy_ratio, BH, W, seq_len, Hq, N);
+    if (log_enabled()) log_printf("  launch lazy_reduce_kernel grid %d x 64 threads", BH);
+    hipLaunchKernelGGL(lazy_reduce_kernel, dim3(BH), dim3(64), 0, st, lazy_rows, lazy_ratio, BH, W, seq_len, Hq,
+                       N);
     return hipGetLastError();
 }
 
