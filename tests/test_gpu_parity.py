@@ -38,6 +38,7 @@ PREFILL_CASES = [
     (2, 130, 6, 3, 64, torch.float32, 0, 7, 130, 21),     # fp32 W=N S=0
     (1, 150, 32, 2, 128, torch.bfloat16, 4, 40, 30, 22),  # G=16
     (1, 97, 16, 1, 64, torch.bfloat16, 4, 20, 9, 23),     # G=16, D=64
+    (1, 2500, 4, 2, 64, torch.bfloat16, 4, 100, 2100, 24),  # W > 1024: the ratio's rows in several LDS rounds
 ]
 
 

@@ -45,6 +45,7 @@ PREFILL_CASES = [
     # long windows: unmasked steps inside every row's window, skipped steps below it
     (800, 8, 2, 128, torch.bfloat16, 4, 250, 32, [800, 640, 300, 33], 37),    # G=4
     (700, 5, 1, 64, torch.bfloat16, 40, 180, 24, [700, 500, 41], 38),         # G=5, D=64, a step of sinks only
+    (2500, 4, 2, 64, torch.bfloat16, 4, 100, 2100, [2500, 1500, 1030], 39),  # W > 1024, shorter sequences than W
 ]
 
 
