@@ -146,3 +146,51 @@ def test_decode_with_score_spikes(L, dtype):
     to, tl, _ = _tol(dtype)
     assert_close("out", np64(out), ref["out"], to)
     assert_close("lse", np64(lse), ref["lse"], tl)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_extreme_spikes_within_the_fp32_dot_product_bound(dtype):
+    """Keys scaled by 10^4 (a spike of 100 applied twice) put logits in the
+    thousands.  There the absolute LSE tolerances (1e-3, 1e-4) lie below what
+    fp32 resolves: a plain fp32 reference misses them by as much.  The bound
+    the arithmetic fixes is the forward error of an fp32 dot product,
+    |fl(q.k) - q.k| <= gamma_D sum_d |q_d k_d| with gamma_D = D u / (1 - D u),
+    u = 2^-24; the LSE is 1-Lipschitz in the max norm of a row's scores, so
+    LSE_i may err by gamma_D max_{j<=i} sum_d |q_id k_jd| / sqrt(D) plus a few
+    units of its own last place, on top of the usual tolerance.  Scores off by
+    at most Delta move each weight exp(s - LSE) by a factor within
+    exp(+-2 Delta), so an output row may err by 2 Delta max|v| on top of its
+    tolerance (for bf16 inputs 3e-2: the bf16 tolerance plus the rounding of
+    bf16 weights).  The ratio keeps the usual tolerance."""
+    B, N, Hq, Hkv, D, S, R, W = 1, 800, 12, 3, 64, 4, 200, 100
+    spikes = [(37, 100.0), (37, 100.0), (300, 100.0), (301, 100.0), (650, 100.0), (650, 100.0), (790, 16.0)]
+    print(f"extreme spikes {dtype}", flush=True)
+    q, k, v = synth.qkv(B, N, Hq, Hkv, D, 201, dtype, spikes=spikes)
+    ref = oracle.prefill(np64(q), np64(k), np64(v), S=S, R=R, W=W, streaming=True)
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    out, lse, rows, ratio = ops.prefill(qd, kd, vd, S, R, W)
+    sout, slse = ops.streaming(qd, kd, vd, S, R)
+    torch.cuda.synchronize()
+    assert float(np.abs(ref["lse"]).max()) > 1e3
+    u = 2.0 ** -24
+    gamma = D * u / (1 - D * u)
+    G = Hq // Hkv
+    qa, ka = np.abs(np64(q)), np.abs(np64(k))
+    tl = TOL_F32 if dtype == torch.float32 else TOL_BF16_LSE
+    to = TOL_F32 if dtype == torch.float32 else 3e-2
+    vmax = float(np.abs(np64(v)).max())
+    for h in range(Hq):
+        mag = qa[0, h] @ ka[0, h // G].T / np.sqrt(D)            # sum_d |q_id k_jd| / sqrt(D)
+        delta = gamma * np.where(np.tri(N, dtype=bool), mag, 0.0).max(axis=1)
+        for name, got, want in (("lse", lse, ref["lse"]), ("slse", slse, ref["slse"])):
+            g_ = np64(got)[0, h]
+            assert np.all(np.isfinite(g_))
+            bound = tl + delta + 8 * u * np.abs(want[0, h])
+            err = np.abs(g_ - want[0, h])
+            assert np.all(err <= bound), f"{name} h{h}: max err/bound {(err / bound).max():.2f}"
+        for name, got, want in (("out", out, ref["out"]), ("sout", sout, ref["sout"])):
+            err = np.abs(np64(got)[0, h] - want[0, h]).max(axis=1)
+            bound = to + 2 * delta * vmax
+            assert np.all(err <= bound), f"{name} h{h}: max err/bound {(err / bound).max():.2f}"
+    tr = TOL_F32 if dtype == torch.float32 else TOL_BF16_RATIO
+    assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], tr)
