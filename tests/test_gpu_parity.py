@@ -39,6 +39,8 @@ PREFILL_CASES = [
     (1, 150, 32, 2, 128, torch.bfloat16, 4, 40, 30, 22),  # G=16
     (1, 97, 16, 1, 64, torch.bfloat16, 4, 20, 9, 23),     # G=16, D=64
     (1, 2500, 4, 2, 64, torch.bfloat16, 4, 100, 2100, 24),  # W > 1024: the ratio's rows in several LDS rounds
+    (1, 1100, 10, 2, 128, torch.bfloat16, 100, 300, 300, 25),  # sinks over two tiles, observed rows reach them
+    (1, 900, 8, 1, 64, torch.bfloat16, 200, 64, 500, 26),      # sinks over two 128-key tiles
 ]
 
 
@@ -109,6 +111,10 @@ STREAM_CASES = [
     (1, 640, 4, 2, 64, torch.bfloat16, 33, 150, 10),   # a step of sinks only, then a mixed one
     (1, 800, 5, 1, 128, torch.bfloat16, 64, 128, 11),  # two whole sink steps
     (1, 300, 32, 2, 128, torch.bfloat16, 4, 60, 12),   # G=16
+    # sinks over two or three 64-key tiles, with windows that reach into them
+    (1, 900, 10, 2, 128, torch.bfloat16, 100, 300, 13),
+    (1, 1500, 8, 1, 64, torch.bfloat16, 130, 200, 14),
+    (2, 700, 6, 3, 128, torch.float32, 150, 90, 15),
 ]
 
 
