@@ -251,6 +251,36 @@ int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float
                                  void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * lt_hybrid_decode_attn_varlen over a paged cache: the keys of every
+ * sequence live in fixed-size pages of one pool, listed by a block table, so
+ * contexts grow a page at a time without moving rows.
+ *   k_pool / v_pool: views whose "batch" index is the pool page:
+ *     data + page * sb + kv_head * sh + row * sn (row < page_size), d
+ *     contiguous; num_pages pages (device memory the caller owns);
+ *   page_size: a power of two in [32, 2^20];
+ *   block_table [B, max_pages] int32 (device): key j of sequence b is row
+ *     j % page_size of pool page block_table[b * max_pages + j / page_size];
+ *     entries of pages past a sequence's context are not read, and an entry
+ *     outside [0, num_pages) is clamped into it (a wrong table reads wrong
+ *     rows, never outside the pool);
+ *   kv_lens [B] int32 (device): sequence b attends to its keys
+ *     [0, kv_lens[b]), kv_lens[b] clamped to [0, max_pages * page_size];
+ *     0 gives out = 0 and lse = -inf;
+ *   ws: at least lt_hybrid_decode_workspace_bytes(B, Hq, Hkv, D,
+ *     max_pages * page_size) bytes.
+ * q, out, lse, dtype and scale as for lt_hybrid_decode_attn.  The result
+ * equals lt_hybrid_decode_attn_varlen over the gathered contiguous caches up
+ * to rounding order.  Errors as for lt_hybrid_decode_attn_varlen, plus
+ * LT_ERR_NULL (block_table), LT_ERR_LAYOUT (block_table or kv_lens not
+ * 4-byte aligned) and LT_ERR_SHAPE (page_size, max_pages, num_pages).
+ */
+int lt_hybrid_decode_attn_paged(int B, int Hq, int Hkv, int D, int dtype, float scale,
+                                const void *q, lt_view k_pool, lt_view v_pool, int page_size,
+                                int num_pages, const int32_t *block_table, int max_pages,
+                                const int32_t *kv_lens, void *out, float *lse, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/*
  * Compaction of a padded variable-length batch: sequence b keeps positions
  * [0,S) and [len_b-R, len_b) of its own length, in the ring slot order of
  * lt_compact_kv_streaming (every row in order when len_b <= S+R); slots at or

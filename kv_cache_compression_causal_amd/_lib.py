@@ -27,7 +27,7 @@ EXPORTS = (
     "lt_prefill_attn_lse_lazy_varlen", "lt_streaming_attn_varlen", "lt_hybrid_decode_attn_varlen",
     "lt_compact_kv_streaming_varlen", "lt_stream_cache_append_varlen", "lt_prefill_attn_lse_lazy_emit",
     "lt_lazy_queue_set_kv_bytes", "lt_lazy_queue_kv_bytes", "lt_kv_accounting",
-    "lt_hybrid_decode_attn_noalloc",
+    "lt_hybrid_decode_attn_noalloc", "lt_hybrid_decode_attn_paged",
 )
 LT_DECODE_NOALLOC_SCRATCH_BYTES = 8 << 20
 
@@ -130,6 +130,10 @@ def load_library(path: str) -> ctypes.CDLL:
                                                LtView, LtView, c_void_p, c_int64, c_void_p, c_void_p,
                                                c_void_p, c_size_t, c_void_p]
     L.lt_hybrid_decode_attn_varlen.restype = c_int
+    L.lt_hybrid_decode_attn_paged.argtypes = [c_int, c_int, c_int, c_int, c_int, ctypes.c_float, c_void_p,
+                                              LtView, LtView, c_int, c_int, c_void_p, c_int, c_void_p,
+                                              c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
+    L.lt_hybrid_decode_attn_paged.restype = c_int
     L.lt_compact_kv_streaming_varlen.argtypes = [LtView, LtView, LtView, LtView, c_int, c_int, c_int, c_int,
                                                  c_int, c_int, c_int, c_void_p, c_void_p]
     L.lt_compact_kv_streaming_varlen.restype = c_int

@@ -259,6 +259,35 @@ def lt_hybrid_decode_attn_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache
                                              _stream(stream)))
 
 
+
+def lt_hybrid_decode_attn_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                block_table: torch.Tensor, kv_lens: torch.Tensor, out: torch.Tensor,
+                                lse: Optional[torch.Tensor], ws: torch.Tensor, scale: float = 0.0,
+                                stream=None) -> None:
+    """Paged caches: k_pool / v_pool [num_pages, Hkv, page_size, D] (any
+    strides with D contiguous), block_table [B, max_pages] and kv_lens [B]
+    int32 on the device; ws sized by lt_hybrid_decode_workspace_bytes(...,
+    max_pages * page_size)."""
+    if not (q.is_contiguous() and out.is_contiguous() and ws.is_contiguous()):
+        raise ValueError("q, out and ws must be contiguous")
+    _same_dtype(q, k_pool, v_pool, out)
+    B, Hq, D = q.shape
+    if tuple(out.shape) != (B, Hq, D) or k_pool.dim() != 4 or k_pool.shape[3] != D \
+            or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("paged decode shape mismatch")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B \
+            or not block_table.is_contiguous() or not block_table.is_cuda:
+        raise ValueError("block_table must be a contiguous int32 [B, max_pages] device tensor")
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != (B, Hq)):
+        raise ValueError("lse must be a contiguous float32 [B, Hq] tensor")
+    num_pages, Hkv, page_size = k_pool.shape[:3]
+    check(lib().lt_hybrid_decode_attn_paged(B, Hq, Hkv, D, _dtype_code(q), float(scale), _ptr(q),
+                                            _view(k_pool), _view(v_pool), page_size, num_pages,
+                                            _dev(block_table), block_table.shape[1],
+                                            _lens(kv_lens, B, "kv_lens"), _ptr(out), _ptr(lse), _ptr(ws),
+                                            ws.numel() * ws.element_size(), _stream(stream)))
+
 def lt_compact_kv_streaming_varlen(k_full: torch.Tensor, v_full: torch.Tensor, k_stream: torch.Tensor,
                                    v_stream: torch.Tensor, seq_lens: torch.Tensor, S: int, R: int,
                                    stream=None) -> None:

@@ -109,21 +109,36 @@ __device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Keys sequence b takes in the end-to-end order of the per-sequence
+// partition: its context, rounded up to whole pages for a paged cache, so
+// that with parts of a whole number of pages every segment starts on a page
+// (and every 32-key step lies inside one page).
+template <bool PAGED>
+__device__ __forceinline__ int64_t ctx_span(const DecodeArgs &a, int b) {
+    const int64_t n = ctx_len(a, b);
+    if constexpr (PAGED) return (n + a.page - 1) >> a.page_shift << a.page_shift;
+    return n;
+}
+
 // Per-sequence contexts (kv_lens): total keys T of one head over the batch
-// and the part size Q = ceil(T/P).
+// and the part size Q = ceil(T/P) (rounded up to whole pages when paged).
 struct Partition {
     int64_t T, Q;
 };
+template <bool PAGED>
 __device__ __forceinline__ Partition partition(const DecodeArgs &a) {
     int64_t T = 0;
-    for (int b = 0; b < a.B; ++b) T += ctx_len(a, b);
-    return Partition{T, T > 0 ? div_nonneg(T + a.n_parts - 1, a.n_parts) : 0};
+    for (int b = 0; b < a.B; ++b) T += ctx_span<PAGED>(a, b);
+    int64_t Q = T > 0 ? div_nonneg(T + a.n_parts - 1, a.n_parts) : 0;
+    if constexpr (PAGED) Q = (Q + a.page - 1) >> a.page_shift << a.page_shift;
+    return Partition{T, Q};
 }
 
 // First key of sequence b in the end-to-end order.
+template <bool PAGED>
 __device__ __forceinline__ int64_t ctx_start(const DecodeArgs &a, int b) {
     int64_t S = 0;
-    for (int i = 0; i < b; ++i) S += ctx_len(a, i);
+    for (int i = 0; i < b; ++i) S += ctx_span<PAGED>(a, i);
     return S;
 }
 
@@ -135,27 +150,54 @@ __device__ __forceinline__ int64_t ctx_start(const DecodeArgs &a, int b) {
 // outside the loop: as straight-line code its loads issue right after the
 // partition arithmetic (inside a loop the compiler hoisted the invariant
 // setup of every segment in front of them, which short layers paid for).
-template <typename F>
+// Paged: a part that reaches only the page padding past a context's end has
+// no keys of that sequence and writes no partial (the merge skips it too).
+template <bool PAGED, typename F>
 __device__ __forceinline__ void for_each_segment(const DecodeArgs &a, int part, F &&f) {
-    const Partition pt = partition(a);
+    const Partition pt = partition<PAGED>(a);
     if (pt.T == 0) return;
     const int64_t g0 = (int64_t)part * pt.Q;
     if (g0 >= pt.T) return;
     const int64_t g1 = g0 + pt.Q < pt.T ? g0 + pt.Q : pt.T;
     // The sequence holding key g0.
     int b = 0;
-    int64_t S = 0, n = ctx_len(a, 0);
+    int64_t S = 0, n = ctx_span<PAGED>(a, 0);
     while (b + 1 < a.B && S + n <= g0) {
         S += n;
-        n = ctx_len(a, ++b);
+        n = ctx_span<PAGED>(a, ++b);
     }
-    f(b, g0 - S, (g1 < S + n ? g1 : S + n) - S, part + b);
+    if constexpr (PAGED) {
+        const int64_t len = ctx_len(a, b);
+        const int64_t kend = (g1 < S + n ? g1 : S + n) - S;
+        if (g0 - S < len) f(b, g0 - S, kend < len ? kend : len, part + b);
+    } else {
+        f(b, g0 - S, (g1 < S + n ? g1 : S + n) - S, part + b);
+    }
     // Sequences after it that the part still reaches.
     for (S += n, ++b; b < a.B && S < g1; ++b) {
-        n = ctx_len(a, b);
-        if (n > 0) f(b, (int64_t)0, (g1 < S + n ? g1 : S + n) - S, part + b);
+        n = ctx_span<PAGED>(a, b);
+        if constexpr (PAGED) {
+            const int64_t len = ctx_len(a, b);
+            const int64_t kend = (g1 < S + n ? g1 : S + n) - S;
+            if (len > 0) f(b, (int64_t)0, kend < len ? kend : len, part + b);
+        } else {
+            if (n > 0) f(b, (int64_t)0, (g1 < S + n ? g1 : S + n) - S, part + b);
+        }
         S += n;
     }
+}
+
+// Pool page of key `key` of sequence b in a paged cache (clamped to the pool,
+// so a table entry out of range reads a wrong page instead of faulting).
+// The table entry is uniform; it is read through the scalar cache and waited
+// for in the same asm block: a vector load would make the wait for it also
+// wait for the step's K and V loads issued before it.
+__device__ __forceinline__ int64_t pool_page(const DecodeArgs &a, int b, int64_t key) {
+    const int *p = a.block_table + ((int64_t)b * a.max_pages + (key >> a.page_shift));
+    int pg;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(pg) : "s"(p));
+    pg = pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+    return pg;
 }
 
 // Partial state of (slot, query head h):
@@ -175,8 +217,11 @@ __device__ __forceinline__ void for_each_segment(const DecodeArgs &a, int part, 
 // streams keys [split*kps, (split+1)*kps) of sequence b, kps = part_keys, and
 // writes slot b*splits + split + b.  Otherwise (kv_lens): workgroup (part,
 // kv head) streams its part of the end-to-end keys (for_each_segment).
-template <int D, bool UNIFORM>
+// PAGED (per-sequence contexts in a page pool): each step's 32 keys lie in
+// one page, whose pool index is read once per step.
+template <int D, bool UNIFORM, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(DecodeArgs a) {
+    static_assert(!(UNIFORM && PAGED), "paged caches take the per-sequence partition");
     constexpr int KS = D / 32;       // 32-dim steps (Q.K)
     constexpr int DB = D / 16;       // 16-dim blocks (O)
     constexpr int STEP = 32;         // keys per step
@@ -233,6 +278,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         bf16x8 vreg[NVL];        // V rows of the next step: row RPI*u + lane/CPR, chunk lane%CPR
         auto issue = [&](int t, int buf) {
             const int64_t key0 = kbeg + (int64_t)t * STEP;
+            if constexpr (PAGED) {
+                // The step's 32 keys lie in one page: rows r = key - key0 of
+                // that page from its row of key0, clamped to the segment's
+                // last key (a uniform bound); the row strides were checked on
+                // the host to keep 31 rows within 32-bit offsets.
+                const int64_t pg = pool_page(a, b, key0), r0 = key0 & (a.page - 1);
+                const bf16 *kp0 = (const bf16 *)a.k + pg * a.k_sb + (int64_t)hk * a.k_sh + r0 * a.k_sn;
+                const bf16 *vp0 = (const bf16 *)a.v + pg * a.v_sb + (int64_t)hk * a.v_sh + r0 * a.v_sn;
+                const int64_t last = kend - 1 - key0;
+                const int lim = last < STEP - 1 ? (int)last : STEP - 1;
+                const int ksn = (int)a.k_sn, vsn = (int)a.v_sn;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int r = kb * 16 + c16 < lim ? kb * 16 + c16 : lim;
+                    const bf16 *kp = kp0 + (r * ksn + (D / 4) * g);
+#pragma unroll
+                    for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
+                }
+#pragma unroll
+                for (int u = 0; u < NVL; ++u) {
+                    const int r = RPI * u + lane / CPR < lim ? RPI * u + lane / CPR : lim;
+                    vreg[u] = load_stream(vp0 + (r * vsn + (lane % CPR) * 8));
+                }
+                return;
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 int64_t key = key0 + kb * 16 + c16;
@@ -385,13 +455,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const int64_t kend = kbeg + a.part_keys < a.kv_len ? kbeg + a.part_keys : a.kv_len;
         if (kbeg < kend) segment(b, kbeg, kend, b * a.splits + split + b);
     } else {
-        for_each_segment(a, (int)blockIdx.x, segment);
+        for_each_segment<PAGED>(a, (int)blockIdx.x, segment);
     }
 }
 
 // fp32: block of 64 lanes per (query head, part), looping over the part's
-// segments; lane owns dims lane, lane+64.
-template <int D, bool UNIFORM>
+// segments; lane owns dims lane, lane+64.  Paged: the pool page is looked up
+// at the segment's first key and at every page boundary.
+template <int D, bool UNIFORM, bool PAGED>
 __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
     constexpr int PER = D / 64;
     const int lane = threadIdx.x;
@@ -406,10 +477,25 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             o[u] = 0.f;
         }
         float m = kNegInf, l = 0.f;
+        const float *kpg = nullptr, *vpg = nullptr;  // paged: the current page's rows of this KV head
         for (int64_t j = kbeg; j < kend; ++j) {
+            const float *kr, *vr;
+            if constexpr (PAGED) {
+                const int64_t r = j & (a.page - 1);
+                if (j == kbeg || r == 0) {
+                    const int64_t pg = pool_page(a, b, j);
+                    kpg = (const float *)a.k + pg * a.k_sb + (int64_t)hk * a.k_sh;
+                    vpg = (const float *)a.v + pg * a.v_sb + (int64_t)hk * a.v_sh;
+                }
+                kr = kpg + r * a.k_sn;
+                vr = vpg + r * a.v_sn;
+            } else {
+                kr = kbase + j * a.k_sn;
+                vr = vbase + j * a.v_sn;
+            }
             float dot = 0.f;
 #pragma unroll
-            for (int u = 0; u < PER; ++u) dot = __builtin_fmaf(q[u], kbase[j * a.k_sn + lane + 64 * u], dot);
+            for (int u = 0; u < PER; ++u) dot = __builtin_fmaf(q[u], kr[lane + 64 * u], dot);
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) dot += __shfl_xor(dot, off);
             const float s = dot * a.c;
@@ -419,7 +505,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
             m = mnew;
             l = l * alpha + p;
 #pragma unroll
-            for (int u = 0; u < PER; ++u) o[u] = __builtin_fmaf(p, vbase[j * a.v_sn + lane + 64 * u], o[u] * alpha);
+            for (int u = 0; u < PER; ++u) o[u] = __builtin_fmaf(p, vr[lane + 64 * u], o[u] * alpha);
         }
         float *dst = a.ws + ((int64_t)ws_slot * a.Hq + h) * (D + 2);
 #pragma unroll
@@ -435,7 +521,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
         const int64_t kend = kbeg + a.part_keys < a.kv_len ? kbeg + a.part_keys : a.kv_len;
         if (kbeg < kend) segment(b, kbeg, kend, b * a.splits + split + b);
     } else {
-        for_each_segment(a, (int)blockIdx.x, segment);
+        for_each_segment<PAGED>(a, (int)blockIdx.x, segment);
     }
 }
 
@@ -445,7 +531,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecodeArgs a) {
 // so each load is a round trip to the shared memory level: all loads of up
 // to CH splits are issued together, and chunks of CH splits are merged
 // online (a running max M with L, O rescaled when it grows).
-template <int D, typename T>
+template <int D, typename T, bool PAGED>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     constexpr int CH = 16;
     read_now(a.ws), read_now(a.o), read_now(a.lse), read_now(a.B), read_now(a.Hq);
@@ -459,8 +545,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     int64_t p0 = (int64_t)b * a.splits;
     int n = a.splits;
     if (a.kv_lens != nullptr) {
-        const Partition pt = partition(a);
-        const int64_t S = ctx_start(a, b), len = ctx_len(a, b);
+        const Partition pt = partition<PAGED>(a);
+        const int64_t S = ctx_start<PAGED>(a, b), len = ctx_len(a, b);
         p0 = len > 0 ? div_nonneg(S, pt.Q) : 0;
         n = len > 0 ? (int)(div_nonneg(S + len - 1, pt.Q) - p0) + 1 : 0;
     }
@@ -536,38 +622,49 @@ size_t decode_ws_bytes(int B, int Hq, int D, int n_parts) {
 namespace {
 // The split kernel, then the merge; each launch is checked, so a refused
 // merge launch is reported even though the split kernel is already queued.
-template <int D>
-hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
+// PAGED: the per-sequence partition over pages of a pool.
+template <int D, bool PAGED>
+hipError_t launch_decode_dp(const DecodeArgs &a, int dtype, hipStream_t st) {
     const bool uni = a.kv_lens == nullptr;
+    const char *kind = PAGED ? "paged" : uni ? "uniform" : "per-sequence";
     if (dtype == LT_BF16) {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv))
                               : dim3((unsigned)a.n_parts, (unsigned)a.Hkv);
         if (log_enabled())
             log_printf("  launch decode_bf16_kernel<D=%d, %s> grid %u x %u x 256 threads (%s), then "
-                       "decode_combine_kernel grid %d x %d threads", D, uni ? "uniform" : "per-sequence", grid.x,
+                       "decode_combine_kernel grid %d x %d threads", D, kind, grid.x,
                        grid.y, uni ? "splits x (sequence, KV head)" : "parts x KV head", a.B * a.Hq, D);
-        if (uni)
-            hipLaunchKernelGGL((decode_bf16_kernel<D, true>), grid, dim3(256), 0, st, a);
+        if (PAGED)
+            hipLaunchKernelGGL((decode_bf16_kernel<D, false, true>), grid, dim3(256), 0, st, a);
+        else if (uni)
+            hipLaunchKernelGGL((decode_bf16_kernel<D, true, false>), grid, dim3(256), 0, st, a);
         else
-            hipLaunchKernelGGL((decode_bf16_kernel<D, false>), grid, dim3(256), 0, st, a);
+            hipLaunchKernelGGL((decode_bf16_kernel<D, false, false>), grid, dim3(256), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_combine_kernel<D, bf16>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
+        hipLaunchKernelGGL((decode_combine_kernel<D, bf16, PAGED>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     } else {
         const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hq))
                               : dim3((unsigned)a.n_parts, (unsigned)a.Hq);
         if (log_enabled())
             log_printf("  launch decode_f32_kernel<D=%d, %s> grid %u x %u x 64 threads, then decode_combine_kernel",
-                       D, uni ? "uniform" : "per-sequence", grid.x, grid.y);
-        if (uni)
-            hipLaunchKernelGGL((decode_f32_kernel<D, true>), grid, dim3(64), 0, st, a);
+                       D, kind, grid.x, grid.y);
+        if (PAGED)
+            hipLaunchKernelGGL((decode_f32_kernel<D, false, true>), grid, dim3(64), 0, st, a);
+        else if (uni)
+            hipLaunchKernelGGL((decode_f32_kernel<D, true, false>), grid, dim3(64), 0, st, a);
         else
-            hipLaunchKernelGGL((decode_f32_kernel<D, false>), grid, dim3(64), 0, st, a);
+            hipLaunchKernelGGL((decode_f32_kernel<D, false, false>), grid, dim3(64), 0, st, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((decode_combine_kernel<D, float>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
+        hipLaunchKernelGGL((decode_combine_kernel<D, float, PAGED>), dim3(a.B * a.Hq), dim3(D), 0, st, a);
     }
     return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_d(const DecodeArgs &a, int dtype, hipStream_t st) {
+    return a.page > 0 ? launch_decode_dp<D, true>(a, dtype, st) : launch_decode_dp<D, false>(a, dtype, st);
 }
 }  // namespace
 

@@ -172,11 +172,20 @@ size_t decode_ws_need(int B, int Hq, int Hkv, int D, int64_t kv_len) {
     return uni > var ? uni : var;
 }
 
+// A paged cache: k_cache / v_cache are page pools (sb = the stride between
+// pages) and key j of sequence b is row j % page_size of pool page
+// block_table[b * max_pages + j / page_size].
+struct PagedCache {
+    const int32_t *block_table;
+    int page_size, max_pages, num_pages;
+};
+
 // ws == nullptr with noalloc: the partial states go to the library's fixed
-// per-GPU scratch array instead of a caller's workspace.
+// per-GPU scratch array instead of a caller's workspace.  pc != nullptr: the
+// cache is paged (kv_lens required, kv_len = max_pages * page_size).
 int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q, lt_view k_cache,
            lt_view v_cache, int64_t kv_len, const int32_t *kv_lens, void *out, float *lse, void *ws,
-           size_t ws_bytes, hipStream_t stream, bool noalloc = false) {
+           size_t ws_bytes, hipStream_t stream, bool noalloc = false, const PagedCache *pc = nullptr) {
     if (dtype != LT_F32 && dtype != LT_BF16) return fail(LT_ERR_DTYPE, "dtype %d unsupported", dtype);
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
@@ -188,6 +197,17 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     if (!aligned16(q) || !aligned16(out)) return fail(LT_ERR_LAYOUT, "q/out not 16-byte aligned");
     int e;
     if ((e = check_view(k_cache, "k_cache", dtype)) || (e = check_view(v_cache, "v_cache", dtype))) return e;
+    if (pc != nullptr) {
+        if (kv_lens == nullptr) return fail(LT_ERR_NULL, "kv_lens is NULL");
+        if (pc->block_table == nullptr) return fail(LT_ERR_NULL, "block_table is NULL");
+        if (((uintptr_t)pc->block_table & 3) || ((uintptr_t)kv_lens & 3))
+            return fail(LT_ERR_LAYOUT, "block_table / kv_lens not 4-byte aligned");
+        const int P = pc->page_size;
+        if (P < 32 || P > (1 << 20) || (P & (P - 1)))
+            return fail(LT_ERR_SHAPE, "page_size %d must be a power of two in [32, 2^20]", P);
+        if (pc->max_pages < 1 || pc->num_pages < 1)
+            return fail(LT_ERR_SHAPE, "max_pages (%d) and num_pages (%d) must be >= 1", pc->max_pages, pc->num_pages);
+    }
     const size_t need = decode_ws_need(B, Hq, Hkv, D, kv_len);
     if (noalloc) {
         if (need > LT_DECODE_NOALLOC_SCRATCH_BYTES)
@@ -218,6 +238,13 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     }
     a.scale = scale > 0.f ? scale : 1.f / sqrtf((float)D);
     a.c = a.scale * 1.4426950408889634f;
+    if (pc != nullptr) {
+        a.block_table = pc->block_table;
+        a.page = pc->page_size;
+        a.page_shift = __builtin_ctz((unsigned)pc->page_size);
+        a.max_pages = pc->max_pages;
+        a.num_pages = pc->num_pages;
+    }
     clear_stale_error();
     return hip_status(lt::launch_decode(a, dtype, stream), "decode launch");
 }
@@ -404,6 +431,21 @@ int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float
     return logged(rc, "lt_hybrid_decode_attn_varlen",
                   "B=%d Hq=%d Hkv=%d D=%d dtype=%d max_kv_len=%lld ws_bytes=%zu stream=%p", B, Hq, Hkv, D, dtype,
                   (long long)max_kv_len, ws_bytes, (void *)stream);
+}
+
+int lt_hybrid_decode_attn_paged(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
+                                lt_view k_pool, lt_view v_pool, int page_size, int num_pages,
+                                const int32_t *block_table, int max_pages, const int32_t *kv_lens, void *out,
+                                float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+    const PagedCache pc{block_table, page_size, max_pages, num_pages};
+    const int64_t kv_len = (int64_t)max_pages * page_size;
+    const int rc = max_pages < 1 || page_size < 1
+                       ? fail(LT_ERR_SHAPE, "max_pages (%d) and page_size (%d) must be >= 1", max_pages, page_size)
+                       : decode(B, Hq, Hkv, D, dtype, scale, q, k_pool, v_pool, kv_len, kv_lens, out, lse, ws,
+                                ws_bytes, stream, false, &pc);
+    return logged(rc, "lt_hybrid_decode_attn_paged",
+                  "B=%d Hq=%d Hkv=%d D=%d dtype=%d page_size=%d num_pages=%d max_pages=%d ws_bytes=%zu stream=%p", B,
+                  Hq, Hkv, D, dtype, page_size, num_pages, max_pages, ws_bytes, (void *)stream);
 }
 
 int lt_compact_kv_streaming(lt_view k_full, lt_view v_full, lt_view k_stream, lt_view v_stream, int B,

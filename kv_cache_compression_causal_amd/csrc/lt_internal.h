@@ -170,6 +170,14 @@ struct DecodeArgs {
     int64_t part_keys;
     int n_parts;
     float scale, c;
+    // Paged caches (page > 0, a power of two >= 32; kv_lens is then set): k
+    // and v are page pools, k_sb / v_sb the stride between pages, k_sh / v_sh
+    // between KV heads within a page, k_sn / v_sn between a page's rows.  Key
+    // j of sequence b sits in row j % page of pool page
+    // block_table[b * max_pages + j / page], clamped to [0, num_pages).
+    // kv_len is max_pages * page.
+    const int *block_table;
+    int page, page_shift, max_pages, num_pages;
 };
 int decode_num_splits(int B, int Hkv, int64_t kv_len);
 int64_t decode_split_keys(int64_t kv_len, int splits);

@@ -109,6 +109,22 @@ def decode_varlen(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     return out, lse
 
 
+
+def decode_paged(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, block_table, kv_lens,
+                 ws: Optional[torch.Tensor] = None, scale: float = 0.0, stream=None):
+    """Decode over paged caches: pools [num_pages, Hkv, page_size, D], a
+    block table [B, max_pages] (tensor or nested lists) and lengths [B]."""
+    B, Hq, D = q.shape
+    table = block_table if isinstance(block_table, torch.Tensor) else torch.tensor(block_table, dtype=torch.int32)
+    table = table.to(device=q.device, dtype=torch.int32).contiguous()
+    if ws is None:
+        ws = decode_workspace(B, Hq, k_pool.shape[1], D, table.shape[1] * k_pool.shape[2], q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+    api.lt_hybrid_decode_attn_paged(q, k_pool, v_pool, table, _device_lens(kv_lens, q.device), out, lse, ws,
+                                    scale, stream)
+    return out, lse
+
 def prefill_emit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, S: int, R: int, W: int, seq_lens=None,
                  slots: Optional[int] = None, scale: float = 0.0, stream=None):
     """Prefill + LSE + lazy ratio that also writes the streaming slice.

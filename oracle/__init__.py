@@ -32,6 +32,9 @@ Readings where the pages are silent:
     slots and the recent rows in ring order (stream_slot);
   * offline selection averages each layer's score over the prompts (fp64,
     prompt order) before taking the top half.
+  * a paged cache (the pages describe none) holds key j of sequence b in
+    row j % page_size of pool page block_table[b][j // page_size]; decode
+    over it is decode over the keys gathered that way (gather_pages).
 
 Parity pins: tests/test_oracle_*.py (brute force in 50-digit arithmetic,
 torch fp64 library routines, closed forms, invariants, exhaustive queue
@@ -249,6 +252,43 @@ def decode_varlen(q, k_cache, v_cache, kv_lens: Sequence[int], scale: Optional[f
         out[b], lse[b] = one["out"][0], one["lse"][0]
     return {"out": out, "lse": lse}
 
+
+
+def gather_pages(pool, block_table, n: int, b: int):
+    """Rows [0, n) of sequence b of a paged cache as one contiguous [Hkv, n, D]
+    array: key j is row j % page_size of pool page block_table[b][j // page_size]
+    (pool [num_pages, Hkv, page_size, D]); an entry outside [0, num_pages) is
+    clamped into it, as the library's paged call documents."""
+    pool = np.asarray(pool)
+    num_pages, Hkv, P, D = pool.shape
+    rows = np.empty((Hkv, n, D), dtype=np.float64)
+    for j in range(n):
+        pg = min(max(int(block_table[b][j // P]), 0), num_pages - 1)
+        rows[:, j, :] = pool[pg, :, j % P, :]
+    return rows
+
+
+def decode_paged(q, k_pool, v_pool, block_table, kv_lens: Sequence[int], scale: Optional[float] = None,
+                 lib=None) -> Dict[str, np.ndarray]:
+    """Decode over paged caches: each sequence's keys gathered from the pools
+    through the block table (gather_pages), then decode_varlen on them.  A
+    length beyond max_pages * page_size is clamped to it; 0 gives out = 0,
+    lse = -inf."""
+    q = _f64(q)
+    B, Hq, D = q.shape
+    P = np.asarray(k_pool).shape[2]
+    cap = len(block_table[0]) * P
+    out = np.zeros((B, Hq, D))
+    lse = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = min(max(int(kv_lens[b]), 0), cap)
+        if n == 0:
+            continue
+        k = gather_pages(k_pool, block_table, n, b)[None]
+        v = gather_pages(v_pool, block_table, n, b)[None]
+        one = decode(q[b:b + 1], k, v, scale=scale, lib=lib)
+        out[b], lse[b] = one["out"][0], one["lse"][0]
+    return {"out": out, "lse": lse}
 
 # ---------------------------------------------------------------------------
 # Host-side selection (pure Python; small inputs by nature: one entry per layer)

@@ -378,6 +378,35 @@ def test_varlen_errors(L):
     assert a(view(), view(), GOOD + 8, GOOD, 2, 2, 128, _lib.LT_BF16, 4, 60, GOOD, None) == _lib.LT_ERR_LAYOUT
 
 
+
+def test_paged_decode_errors(L):
+    """lt_hybrid_decode_attn_paged validates the pools, the table, the page
+    geometry and the workspace (sized for max_pages * page_size keys) before
+    any launch; every case below fails first."""
+    f = L.lt_hybrid_decode_attn_paged
+    bf = _lib.LT_BF16
+    n = ctypes.c_size_t()
+    assert L.lt_hybrid_decode_workspace_bytes(4, 16, 2, 128, 64 * 256, ctypes.byref(n)) == 0
+    need = n.value
+
+    def call(B=4, Hq=16, Hkv=2, D=128, dt=bf, q=GOOD, k=None, v=None, P=256, npages=300, table=GOOD,
+             maxp=64, lens=GOOD, ws=GOOD, wsb=need):
+        return f(B, Hq, Hkv, D, dt, 0.0, q, k or view(), v or view(), P, npages, table, maxp, lens, GOOD, None,
+                 ws, wsb, None)
+    assert call(table=None) == _lib.LT_ERR_NULL
+    assert call(lens=None) == _lib.LT_ERR_NULL
+    assert call(table=GOOD + 2) == _lib.LT_ERR_LAYOUT
+    assert call(lens=GOOD + 2) == _lib.LT_ERR_LAYOUT
+    for P in (16, 48, 0, -256, 1 << 21):
+        assert call(P=P) == _lib.LT_ERR_SHAPE, P
+    assert call(maxp=0) == _lib.LT_ERR_SHAPE
+    assert call(npages=0) == _lib.LT_ERR_SHAPE
+    assert call(wsb=need - 1) == _lib.LT_ERR_WORKSPACE
+    assert call(D=96) == _lib.LT_ERR_DTYPE
+    assert call(Hq=17) == _lib.LT_ERR_SHAPE
+    assert call(k=view(sn=100)) == _lib.LT_ERR_LAYOUT
+    assert call(q=None) == _lib.LT_ERR_NULL
+
 def test_noalloc_decode_validates_before_touching_the_gpu(L):
     """lt_hybrid_decode_attn_noalloc checks its arguments, and that the
     partial states fit the library's scratch array, before anything touches
