@@ -400,6 +400,7 @@ def test_lt_log_prints_each_launch():
 
 def test_layer_calls_captured_in_a_graph():
     """Prefill + lazy ratio, streaming, compaction and decode of one layer
+    (and a paged decode over the layer's K/V read as 32-row pages)
     captured in one HIP graph on a side stream, replayed three times after
     new inputs were copied in eagerly (with unrelated eager work and a
     synchronisation between replays): every replay gives the eager calls'
@@ -421,7 +422,15 @@ def test_layer_calls_captured_in_a_graph():
     dout = torch.empty_like(qt)
     dlse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
     ws = ops.decode_workspace(B, Hq, Hkv, D, S + R, DEV)
-    outs = (out, lse, rows, ratio, sout, slse, ks, vs, dout, dlse)
+    P, npg = 32, N // 32                                       # k, v [1, Hkv, N, D] as a pool of 32-row pages
+    kp = torch.as_strided(k, (npg, Hkv, P, D), (P * D, N * D, D, 1))
+    vp = torch.as_strided(v, (npg, Hkv, P, D), (P * D, N * D, D, 1))
+    table = torch.as_tensor(np.random.default_rng(65).permutation(npg)[None], dtype=torch.int32).to(DEV)
+    plens = torch.tensor([npg * P - 5], device=DEV, dtype=torch.int32)
+    pws = ops.decode_workspace(B, Hq, Hkv, D, npg * P, DEV)
+    pout = torch.empty_like(qt)
+    plse = torch.empty(B, Hq, device=DEV, dtype=torch.float32)
+    outs = (out, lse, rows, ratio, sout, slse, ks, vs, dout, dlse, pout, plse)
 
     def layer(st):
         api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio, 0.0, st)
@@ -429,6 +438,7 @@ def test_layer_calls_captured_in_a_graph():
         api.lt_compact_kv_streaming(k, v, ks, vs, S, R, st)
         qt.copy_(q[:, :, -1])
         api.lt_hybrid_decode_attn(qt, ks, vs, S + R, dout, dlse, ws, 0.0, st)
+        api.lt_hybrid_decode_attn_paged(qt, kp, vp, table, plens, pout, plse, pws, 0.0, st)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -458,6 +468,9 @@ def test_layer_calls_captured_in_a_graph():
     assert_close("out", np64(out), ref["out"], TOL_BF16_OUT)
     assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], TOL_BF16_RATIO)
     assert_close("sout", np64(sout), ref["sout"], TOL_BF16_OUT)
+    pref = oracle.decode_paged(np64(qt), np64(kp), np64(vp), table.cpu().numpy(), [npg * P - 5])
+    assert_close("paged out", np64(pout), pref["out"], TOL_BF16_OUT)
+    assert_close("paged lse", np64(plse), pref["lse"], TOL_BF16_LSE)
 
 
 def test_calls_on_two_streams_at_once():
