@@ -116,6 +116,34 @@ def test_decode100k_varlen_full_size():
         assert_close(f"decode lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
 
 
+
+def test_decode100k_paged_full_size():
+    """The same full layer and contexts read as a pool of 32-row pages (page
+    b * Hkv * rows / 32 + c is rows [32c, 32c + 32) of sequence b, the head
+    stride kept), each sequence's pages listed in a shuffled order, as the
+    bench times it: three (batch, KV head) groups against the oracle's decode
+    over the keys in table order."""
+    w, lens = synth.DECODE100K, synth.DECODE100K_VARLEN_LENS
+    q, k, v = synth.decode_layer(0, w, device=DEV)
+    P, rows = 32, k.shape[2]
+    ppb = rows // P
+    npg = (w.B - 1) * w.Hkv * ppb + ppb
+    kp = torch.as_strided(k, (npg, w.Hkv, P, w.D), (P * w.D, rows * w.D, w.D, 1))
+    vp = torch.as_strided(v, (npg, w.Hkv, P, w.D), (P * w.D, rows * w.D, w.D, 1))
+    rng = np.random.default_rng(5)
+    table = np.stack([b * w.Hkv * ppb + rng.permutation(ppb) for b in range(w.B)]).astype(np.int32)
+    out, lse = ops.decode_paged(q, kp, vp, torch.as_tensor(table), lens)
+    torch.cuda.synchronize()
+    G = w.Hq // w.Hkv
+    for b, hk in [(0, 0), (w.B - 1, w.Hkv - 1), (3, 5)]:
+        n = lens[b]
+        pages = table[b, :-(-n // P)] - b * w.Hkv * ppb         # the sequence's own page numbers, in table order
+        idx = torch.as_tensor((pages[:, None] * P + np.arange(P)[None]).reshape(-1)[:n], device=DEV)
+        kk, vv = k[b, hk][idx], v[b, hk][idx]
+        r = oracle.decode(np64(q[b:b + 1, hk * G:(hk + 1) * G]), np64(kk)[None, None], np64(vv)[None, None])
+        assert_close(f"paged out b{b} hk{hk}", np64(out[b:b + 1, hk * G:(hk + 1) * G]), r["out"], TOL_BF16_OUT)
+        assert_close(f"paged lse b{b} hk{hk}", np64(lse[b:b + 1, hk * G:(hk + 1) * G]), r["lse"], TOL_BF16_LSE)
+
 def _check_selection_end_to_end(want_scores, got_scores, evicted, is_streaming, capacity, policy):
     """The selection made on the GPU's ratios against the oracle's fp64 layer
     scores.  Every GPU score is within the ratio tolerance of the oracle's.
