@@ -257,7 +257,7 @@ int lt_hybrid_decode_attn_varlen(int B, int Hq, int Hkv, int D, int dtype, float
  *   k_pool / v_pool: views whose "batch" index is the pool page:
  *     data + page * sb + kv_head * sh + row * sn (row < page_size), d
  *     contiguous; num_pages pages (device memory the caller owns);
- *   page_size: a power of two in [32, 2^20];
+ *   page_size: a power of two in [16, 2^20];
  *   block_table [B, max_pages] int32 (device): key j of sequence b is row
  *     j % page_size of pool page block_table[b * max_pages + j / page_size];
  *     entries of pages past a sequence's context are not read, and an entry

@@ -112,7 +112,7 @@ __device__ __forceinline__ int64_t div_nonneg(int64_t x, int64_t y) {
 // Keys sequence b takes in the end-to-end order of the per-sequence
 // partition: its context, rounded up to whole pages for a paged cache, so
 // that with parts of a whole number of pages every segment starts on a page
-// (and every 32-key step lies inside one page).
+// (and every 16-key half of a 32-key step lies inside one page).
 template <bool PAGED>
 __device__ __forceinline__ int64_t ctx_span(const DecodeArgs &a, int b) {
     const int64_t n = ctx_len(a, b);
@@ -217,8 +217,9 @@ __device__ __forceinline__ int64_t pool_page(const DecodeArgs &a, int b, int64_t
 // streams keys [split*kps, (split+1)*kps) of sequence b, kps = part_keys, and
 // writes slot b*splits + split + b.  Otherwise (kv_lens): workgroup (part,
 // kv head) streams its part of the end-to-end keys (for_each_segment).
-// PAGED (per-sequence contexts in a page pool): each step's 32 keys lie in
-// one page, whose pool index is read once per step.
+// PAGED (per-sequence contexts in a page pool): each 16-key half of a step
+// lies in one page, whose pool index is read once per step (twice with
+// 16-row pages).
 template <int D, bool UNIFORM, bool PAGED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_bf16_kernel(DecodeArgs a) {
     static_assert(!(UNIFORM && PAGED), "paged caches take the per-sequence partition");
@@ -279,27 +280,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         auto issue = [&](int t, int buf) {
             const int64_t key0 = kbeg + (int64_t)t * STEP;
             if constexpr (PAGED) {
-                // The step's 32 keys lie in one page: rows r = key - key0 of
-                // that page from its row of key0, clamped to the segment's
-                // last key (a uniform bound); the row strides were checked on
-                // the host to keep 31 rows within 32-bit offsets.
+                // Rows r = key - key0 of the step, clamped to the segment's
+                // last key (a uniform bound), are read from the page of key0
+                // at its row of key0.  Pages of 32 rows or more hold the whole
+                // step.  16-row pages hold one 16-key half each: the second
+                // half (r >= 16, the K operand's second block and the second
+                // half of the V loads) then comes from the page of key0 + 16,
+                // looked up only when that half has keys.  The row strides
+                // were checked on the host to keep 31 rows within 32-bit
+                // offsets.
                 const int64_t pg = pool_page(a, b, key0), r0 = key0 & (a.page - 1);
-                const bf16 *kp0 = (const bf16 *)a.k + pg * a.k_sb + (int64_t)hk * a.k_sh + r0 * a.k_sn;
-                const bf16 *vp0 = (const bf16 *)a.v + pg * a.v_sb + (int64_t)hk * a.v_sh + r0 * a.v_sn;
+                const int64_t kA = pg * a.k_sb + (int64_t)hk * a.k_sh + r0 * a.k_sn;
+                const int64_t vA = pg * a.v_sb + (int64_t)hk * a.v_sh + r0 * a.v_sn;
+                int64_t kB = kA, vB = vA;  // element offsets of row 0 of the step, for rows r >= 16
+                if (a.page_shift == 4 && key0 + 16 < kend) {
+                    const int64_t pg2 = pool_page(a, b, key0 + 16);
+                    kB = pg2 * a.k_sb + (int64_t)hk * a.k_sh - 16 * a.k_sn;
+                    vB = pg2 * a.v_sb + (int64_t)hk * a.v_sh - 16 * a.v_sn;
+                }
                 const int64_t last = kend - 1 - key0;
                 const int lim = last < STEP - 1 ? (int)last : STEP - 1;
                 const int ksn = (int)a.k_sn, vsn = (int)a.v_sn;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
                     const int r = kb * 16 + c16 < lim ? kb * 16 + c16 : lim;
-                    const bf16 *kp = kp0 + (r * ksn + (D / 4) * g);
+                    const bf16 *kp = (const bf16 *)a.k + (kb == 0 ? kA : kB) + (r * ksn + (D / 4) * g);
 #pragma unroll
                     for (int u = 0; u < KPL; ++u) kreg[buf][kb][u] = *(const bf16x8 *)(kp + 8 * u);
                 }
 #pragma unroll
                 for (int u = 0; u < NVL; ++u) {
                     const int r = RPI * u + lane / CPR < lim ? RPI * u + lane / CPR : lim;
-                    vreg[u] = load_stream(vp0 + (r * vsn + (lane % CPR) * 8));
+                    vreg[u] = load_stream((const bf16 *)a.v + (RPI * u < 16 ? vA : vB) + (r * vsn + (lane % CPR) * 8));
                 }
                 return;
             }

@@ -203,8 +203,8 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
         if (((uintptr_t)pc->block_table & 3) || ((uintptr_t)kv_lens & 3))
             return fail(LT_ERR_LAYOUT, "block_table / kv_lens not 4-byte aligned");
         const int P = pc->page_size;
-        if (P < 32 || P > (1 << 20) || (P & (P - 1)))
-            return fail(LT_ERR_SHAPE, "page_size %d must be a power of two in [32, 2^20]", P);
+        if (P < 16 || P > (1 << 20) || (P & (P - 1)))
+            return fail(LT_ERR_SHAPE, "page_size %d must be a power of two in [16, 2^20]", P);
         if (pc->max_pages < 1 || pc->num_pages < 1)
             return fail(LT_ERR_SHAPE, "max_pages (%d) and num_pages (%d) must be >= 1", pc->max_pages, pc->num_pages);
     }

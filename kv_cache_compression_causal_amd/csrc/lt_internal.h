@@ -170,7 +170,7 @@ struct DecodeArgs {
     int64_t part_keys;
     int n_parts;
     float scale, c;
-    // Paged caches (page > 0, a power of two >= 32; kv_lens is then set): k
+    // Paged caches (page > 0, a power of two >= 16; kv_lens is then set): k
     // and v are page pools, k_sb / v_sb the stride between pages, k_sh / v_sh
     // between KV heads within a page, k_sn / v_sn between a page's rows.  Key
     // j of sequence b sits in row j % page of pool page

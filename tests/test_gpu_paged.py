@@ -65,7 +65,7 @@ def _cases(n=40, seed=555):
         dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
         if dtype == torch.float32 and G > 8:
             G = 8
-        P = int(rng.choice([32, 64, 128, 256]))
+        P = int(rng.choice([16, 32, 64, 128, 256]))
         special = [0, 1, P - 1, P, P + 1, 2 * P + 31]
         lens = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 3000))
                 for _ in range(B)]
@@ -83,6 +83,14 @@ def test_paged_decode_random(B, Hq, Hkv, D, P, lens, dtype, seed):
     print(f"paged decode B{B} Hq{Hq} Hkv{Hkv} D{D} page {P} lens {list(lens)} {dtype} seed {seed}", flush=True)
     q, kp, vp, table = _paged_inputs(B, Hq, Hkv, D, P, list(lens), dtype, seed)
     _check(q, kp, vp, table, list(lens), dtype)
+
+
+def test_paged_decode_long_contexts_in_16_row_pages():
+    B, Hq, Hkv, D, P = 2, 16, 2, 128, 16
+    lens = [9000, 4111]
+    print(f"paged decode B{B} Hq{Hq} Hkv{Hkv} D{D} page {P} lens {lens}", flush=True)
+    q, kp, vp, table = _paged_inputs(B, Hq, Hkv, D, P, lens, torch.bfloat16, 802, extra_pages=7)
+    _check(q, kp, vp, table, lens, torch.bfloat16)
 
 
 def test_paged_decode_long_contexts_in_large_pages():
