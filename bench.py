@@ -448,45 +448,45 @@ class Bench:
             # cache read as a pool of PAGE-row pages (page b * Hkv * rows / PAGE
             # + c is rows [c * PAGE, (c + 1) * PAGE) of sequence b, the head
             # stride kept), and each sequence's pages listed in a shuffled
-            # order: as many keys per sequence as the varlen step, one table
-            # lookup per 32-key step (PAGE = 32 divides both cache sizes).
-            PAGE = 32
-            assert all(n % PAGE == 0 for n in lens)
+            # order: as many keys per sequence as the varlen step.  Pages of 32
+            # rows take one table lookup per 32-key step, pages of 16 two.
             prng = np.random.default_rng(dw.seed)
-
-            def pool_of(t, rows):
-                ppb = rows // PAGE
-                n_pages = (dw.B - 1) * dw.Hkv * ppb + ppb
-                return torch.as_strided(t, (n_pages, dw.Hkv, PAGE, dw.D), (PAGE * dw.D, rows * dw.D, dw.D, 1))
-
-            def table_of(rows):
-                ppb = rows // PAGE
-                return torch.tensor(np.stack([b * dw.Hkv * ppb + prng.permutation(ppb) for b in range(dw.B)]),
-                                    dtype=torch.int32, device=self.dev)
-
-            tab_full, tab_stream = table_of(lens[0]), table_of(lens[-1])
-            kpools = [pool_of(ks_[l], lens[l]) for l in range(L)]
-            vpools = [pool_of(vs_[l], lens[l]) for l in range(L)]
-
-            def decode_all_paged(st):
-                for l in range(L):
-                    api.lt_hybrid_decode_attn_paged(qs[l], kpools[l], vpools[l],
-                                                    tab_full if l < nfull else tab_stream,
-                                                    full_lens if l < nfull else stream_lens, outs[l], lses[l], ws,
-                                                    0.0, st)
-
-            pgraph = graph_of(decode_all_paged)
-            pts = self.time_each(pgraph.replay, self.reps, warm=3)
-            pd_ms = median(pts)
-            pgbps = vbytes / (pd_ms * 1e-3) / 1e9
-            log(f"paged decode: {pd_ms:.3f} ms/step, {pgbps:.1f} GB/s")
             res["decode_paged"] = {
-                "workload": f"the decode100k-varlen step over paged caches: pages of {PAGE} rows, each sequence's "
-                            "pages in a shuffled order of the pool (lt_hybrid_decode_attn_paged)",
-                "ms_per_step_median": round(pd_ms, 4), "gbps": round(pgbps, 1),
-                "frac_hbm_peak": round(pgbps * 1e9 / PEAK_HBM, 4), "bytes_per_step": vbytes,
-                "time_vs_varlen": round(pd_ms / vd_ms, 4)}
-            del pgraph, kpools, vpools
+                "workload": "the decode100k-varlen step over paged caches, each sequence's pages in a shuffled "
+                            "order of the pool (lt_hybrid_decode_attn_paged)", "bytes_per_step": vbytes}
+            for PAGE in (32, 16):
+                assert all(n % PAGE == 0 for n in lens)
+
+                def pool_of(t, rows):
+                    ppb = rows // PAGE
+                    n_pages = (dw.B - 1) * dw.Hkv * ppb + ppb
+                    return torch.as_strided(t, (n_pages, dw.Hkv, PAGE, dw.D), (PAGE * dw.D, rows * dw.D, dw.D, 1))
+
+                def table_of(rows):
+                    ppb = rows // PAGE
+                    return torch.tensor(np.stack([b * dw.Hkv * ppb + prng.permutation(ppb) for b in range(dw.B)]),
+                                        dtype=torch.int32, device=self.dev)
+
+                tab_full, tab_stream = table_of(lens[0]), table_of(lens[-1])
+                kpools = [pool_of(ks_[l], lens[l]) for l in range(L)]
+                vpools = [pool_of(vs_[l], lens[l]) for l in range(L)]
+
+                def decode_all_paged(st):
+                    for l in range(L):
+                        api.lt_hybrid_decode_attn_paged(qs[l], kpools[l], vpools[l],
+                                                        tab_full if l < nfull else tab_stream,
+                                                        full_lens if l < nfull else stream_lens, outs[l], lses[l],
+                                                        ws, 0.0, st)
+
+                pgraph = graph_of(decode_all_paged)
+                pts = self.time_each(pgraph.replay, self.reps, warm=3)
+                pd_ms = median(pts)
+                pgbps = vbytes / (pd_ms * 1e-3) / 1e9
+                log(f"paged decode, {PAGE}-row pages: {pd_ms:.3f} ms/step, {pgbps:.1f} GB/s")
+                res["decode_paged"][f"page_{PAGE}"] = {
+                    "ms_per_step_median": round(pd_ms, 4), "gbps": round(pgbps, 1),
+                    "frac_hbm_peak": round(pgbps * 1e9 / PEAK_HBM, 4), "time_vs_varlen": round(pd_ms / vd_ms, 4)}
+                del pgraph, kpools, vpools
         del qs, ks_, vs_, outs, lses, ws
         torch.cuda.empty_cache()
         return res
