@@ -540,8 +540,21 @@ class Bench:
         layer_inputs = lambda l: layers[l]
         fl_layer = prefill_flop(dw.B, dw.Hq, dw.N, dw.D) + lazy_flop(dw.B, dw.Hq, dw.N, dw.D, dw.S, dw.R, dw.W)
         MiB = 1 << 20
-        # a short untimed pass (warm code paths and allocator), then the timed pass
-        driver.run(layer_inputs, min(4, L64), min(2, C), dw.S, dw.R, dw.W)
+        # one untimed pass like the timed one (its allocations of the evicted
+        # layers' streaming caches fill torch's caching allocator, whose
+        # first-time allocations otherwise stall the timed pass's host loop)
+        # and the clock warm-up of the other prefill legs (generating 28 GiB of
+        # inputs leaves the chip at a lower clock than a matrix-core load
+        # holds), then the timed pass
+        driver.run(layer_inputs, L64, C, dw.S, dw.R, dw.W)
+        q0, k0, v0 = layers[0]
+        o0 = torch.empty_like(q0)
+        l0 = torch.empty(dw.B, dw.Hq, dw.N, device=self.dev, dtype=torch.float32)
+        r0 = torch.empty(dw.B, dw.Hq, dw.W, device=self.dev, dtype=torch.float32)
+        a0 = torch.empty(dw.B, dw.Hq, device=self.dev, dtype=torch.float32)
+        self.warm_clock(lambda: self.api.lt_prefill_attn_lse_lazy(q0, k0, v0, o0, l0, dw.S, dw.R, dw.W, r0, a0, 0.0,
+                                                                  self.stream))
+        del o0, l0, r0, a0
         log("driver64: timed pass")
         res = driver.run(layer_inputs, L64, C, dw.S, dw.R, dw.W, timing=True)
         srt = sorted(res.layer_score)
