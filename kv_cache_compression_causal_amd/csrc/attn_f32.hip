@@ -9,15 +9,22 @@
 // recent keys; project page, "Introduction" -- converted layers run streaming
 // attention.
 //
-// Work decomposition.  A workgroup of four waves owns ROWS = 16 consecutive
+// Work decomposition.  A workgroup of NW waves owns ROWS = 16 consecutive
 // query rows of one (sequence, query head); each row is spread over LPR = 4
 // lanes of a wave holding D/4 dims of its query and output each, so a dot
-// product is four partial sums joined by two quad permutes.  The four waves
-// take every fourth key tile of the rows' key range (split-K): each stages
+// product is four partial sums joined by two quad permutes.  The NW waves
+// take every NW-th key tile of the rows' key range (split-K): each stages
 // its tiles in an LDS region of its own and keeps its own running max, sum
-// and lazy-ratio numerator, and the four partial states are merged through
+// and lazy-ratio numerator, and the NW partial states are merged through
 // LDS at the end.  Workgroups and key work are both small and many, so a
 // layer of a few hundred rows (latency-bound) spreads over the whole chip.
+// Full attention takes 16 waves (4 KiB K and V tiles per wave, one
+// workgroup per CU, four waves per SIMD): a row's keys grow with its
+// position, and the longest rows bound the launch.  Streaming attention,
+// whose rows see at most S + R keys, takes 4 waves (8 KiB tiles); with 16,
+// most waves of a band workgroup had no tile.  (At 512 tokens 16 waves ran
+// the prefill in 21 against 37 us, at 8K tokens 3.4 against 4.6 ms; 4 waves
+// kept streaming at 186 against 253 us.)
 #include "lt_internal.h"
 
 namespace lt {
@@ -25,7 +32,6 @@ namespace {
 
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kWaves = 4;
 constexpr int kLPR = 4;               // lanes per query row
 constexpr int kRows = 64 / kLPR;      // query rows per workgroup (and per wave)
 constexpr int kChunk = 8;             // keys per online-softmax update
@@ -39,14 +45,22 @@ __device__ __forceinline__ float quad_sum(float x) {
     return x;
 }
 
+// Waves per workgroup of each mode (see above).
+constexpr int waves_of(int mode) { return mode == MODE_STREAM ? 4 : 16; }
+
 template <int D, int MODE>
-__global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * waves_of(MODE)) void attn_f32_kernel(AttnArgs a) {
+    constexpr int kWaves = waves_of(MODE);
     constexpr int DPL = D / kLPR;         // dims per lane
-    constexpr int TK = 2048 / D;          // keys per tile (8 KiB of K, 8 KiB of V)
+    constexpr int TK = (kWaves > 4 ? 1024 : 2048) / D;  // keys per tile (4 or 8 KiB of K, the same of V)
     constexpr int TILE = TK * D;
     constexpr bool LAZY = MODE == MODE_FULL_LAZY;
-    // Per wave: its K and V tile; after the key loop, the merge buffers.
-    __shared__ __attribute__((aligned(16))) float smem[kWaves * 2 * TILE];
+    // Per wave: its K and V tile; after the key loop, the merge buffers (each
+    // wave's partial outputs, then each row's m, l and lazy numerator per
+    // wave), which at 16 waves and D = 128 need more than the tiles.
+    constexpr int TILES = kWaves * 2 * TILE;
+    constexpr int MERGE = kWaves * 64 * DPL + kWaves * kRows * 3;
+    __shared__ __attribute__((aligned(16))) float smem[TILES > MERGE ? TILES : MERGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
 template <int D>
 hipError_t launch_d(const AttnArgs &a, int mode, hipStream_t st) {
     dim3 grid((unsigned)((a.N + kRows - 1) / kRows), (unsigned)(a.B * a.Hq));
-    dim3 block(64 * kWaves);
+    dim3 block(64 * waves_of(mode));
     if (log_enabled())
         log_printf("  launch attn_f32_kernel<D=%d, mode=%s> grid %u x %u x %u threads", D,
                    mode == MODE_FULL ? "full" : mode == MODE_FULL_LAZY ? "full+lazy" : "stream", grid.x, grid.y,
