@@ -402,10 +402,11 @@ def test_layer_calls_captured_in_a_graph():
     """Prefill + lazy ratio, streaming, compaction and decode of one layer
     (and a paged decode over the layer's K/V read as 32-row pages)
     captured in one HIP graph on a side stream, replayed three times after
-    new inputs were copied in eagerly (with unrelated eager work and a
-    synchronisation between replays): every replay gives the eager calls'
-    bits on the same inputs.  The library issues no memset or allocation,
-    so nothing in the graph depends on capture-time state."""
+    new inputs, a new page table and a new length were copied in eagerly
+    (with unrelated eager work and a synchronisation between replays):
+    every replay gives the eager calls' bits on the same inputs.  The
+    library issues no memset or allocation, so nothing in the graph depends
+    on capture-time state."""
     from kv_cache_compression_causal_amd import api
     B, N, Hq, Hkv, D, S, R, W = 1, 700, 8, 2, 128, 4, 100, 40
     G = Hq // Hkv
@@ -453,6 +454,10 @@ def test_layer_calls_captured_in_a_graph():
         print(f"graph replay, inputs seed {seed}", flush=True)
         nq, nk, nv = synth.qkv(B, N, Hq, Hkv, D, seed, torch.bfloat16)
         q.copy_(nq), k.copy_(nk), v.copy_(nv)
+        # a new page order and length for the paged decode (read through the
+        # scalar cache: a stale entry would make the replay differ from eager)
+        table.copy_(torch.as_tensor(np.random.default_rng(seed).permutation(npg)[None], dtype=torch.int32))
+        plens.fill_(npg * P - seed % 7)
         _ = (q.float() * 2.0).sum()                           # unrelated eager work between replays
         torch.cuda.synchronize()
         graph.replay()
@@ -468,7 +473,7 @@ def test_layer_calls_captured_in_a_graph():
     assert_close("out", np64(out), ref["out"], TOL_BF16_OUT)
     assert_close("lazy_ratio", np64(ratio), ref["lazy_ratio"], TOL_BF16_RATIO)
     assert_close("sout", np64(sout), ref["sout"], TOL_BF16_OUT)
-    pref = oracle.decode_paged(np64(qt), np64(kp), np64(vp), table.cpu().numpy(), [npg * P - 5])
+    pref = oracle.decode_paged(np64(qt), np64(kp), np64(vp), table.cpu().numpy(), [int(plens.item())])
     assert_close("paged out", np64(pout), pref["out"], TOL_BF16_OUT)
     assert_close("paged lse", np64(plse), pref["lse"], TOL_BF16_LSE)
 
