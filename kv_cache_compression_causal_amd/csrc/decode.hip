@@ -243,6 +243,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, c16 = lane & 15;
     const int hk = UNIFORM ? (int)(blockIdx.y % a.Hkv) : (int)blockIdx.y;
+    // Query heads hk*G + hc .. + ncol - 1 of the group: the 16 columns of the
+    // products hold at most 16 heads, so a group of more (G > 16) is served
+    // in chunks of 16, one per grid z (each chunk streams the keys itself).
+    const int hc = 16 * (int)blockIdx.z;
+    const int ncol = a.G - hc < 16 ? a.G - hc : 16;
     poison_lds<256>(smem, (int)sizeof(smem), tid);
     poison_lds<256>(red_m, (int)sizeof(red_m), tid);
     poison_lds<256>(red_l, (int)sizeof(red_l), tid);
@@ -266,8 +271,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         // dims (D/4)g + 8ks .. +7 of step ks -- the same dim order as the K operand.
         bf16x8 qreg[KS];
         {
-            const bool col_ok = c16 < G;
-            const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + (col_ok ? c16 : 0)) * D + (D / 4) * g;
+            const bool col_ok = c16 < ncol;
+            const bf16 *qp = (const bf16 *)a.q + ((int64_t)b * a.Hq + hk * G + hc + (col_ok ? c16 : 0)) * D + (D / 4) * g;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks) {
                 bf16x8 v = *(const bf16x8 *)(qp + 8 * ks);
@@ -440,7 +445,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
         for (int r = 0; r < 4; ++r) red_o[wave][c16][db * 16 + 4 * g + r] = o[db][r];
     __syncthreads();
-    for (int e = tid; e < G * D; e += 256) {
+    for (int e = tid; e < ncol * D; e += 256) {
         const int col = e / D, d = e % D;
         float M = kNegInf;
 #pragma unroll
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
             L += f * red_l[w][col];
             O += f * red_o[w][col][d];
         }
-        float *dst = a.ws + ((int64_t)ws_slot * a.Hq + hk * G + col) * (D + 2);
+        float *dst = a.ws + ((int64_t)ws_slot * a.Hq + hk * G + hc + col) * (D + 2);
         dst[d] = O / L;
         if (d == 0) {
             dst[D] = M;
@@ -640,12 +645,14 @@ hipError_t launch_decode_dp(const DecodeArgs &a, int dtype, hipStream_t st) {
     const bool uni = a.kv_lens == nullptr;
     const char *kind = PAGED ? "paged" : uni ? "uniform" : "per-sequence";
     if (dtype == LT_BF16) {
-        const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv))
-                              : dim3((unsigned)a.n_parts, (unsigned)a.Hkv);
+        const unsigned chunks = (unsigned)((a.G + 15) / 16);  // query-head chunks of 16 per KV head
+        const dim3 grid = uni ? dim3((unsigned)a.splits, (unsigned)(a.B * a.Hkv), chunks)
+                              : dim3((unsigned)a.n_parts, (unsigned)a.Hkv, chunks);
         if (log_enabled())
-            log_printf("  launch decode_bf16_kernel<D=%d, %s> grid %u x %u x 256 threads (%s), then "
-                       "decode_combine_kernel grid %d x %d threads", D, kind, grid.x,
-                       grid.y, uni ? "splits x (sequence, KV head)" : "parts x KV head", a.B * a.Hq, D);
+            log_printf("  launch decode_bf16_kernel<D=%d, %s> grid %u x %u x %u x 256 threads (%s), then "
+                       "decode_combine_kernel grid %d x %d threads", D, kind, grid.x, grid.y, grid.z,
+                       uni ? "splits x (sequence, KV head) x head chunks" : "parts x KV head x head chunks",
+                       a.B * a.Hq, D);
         if (PAGED)
             hipLaunchKernelGGL((decode_bf16_kernel<D, false, true>), grid, dim3(256), 0, st, a);
         else if (uni)

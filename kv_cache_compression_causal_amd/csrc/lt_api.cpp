@@ -190,7 +190,6 @@ int decode(int B, int Hq, int Hkv, int D, int dtype, float scale, const void *q,
     if (D != 64 && D != 128) return fail(LT_ERR_DTYPE, "head dim %d unsupported (64 or 128)", D);
     if (B < 1 || Hq < 1 || Hkv < 1 || kv_len < 1 || Hq % Hkv)
         return fail(LT_ERR_SHAPE, "bad decode sizes (B=%d Hq=%d Hkv=%d kv_len=%lld)", B, Hq, Hkv, (long long)kv_len);
-    if (dtype == LT_BF16 && Hq / Hkv > 16) return fail(LT_ERR_SHAPE, "bf16 decode supports Hq/Hkv <= 16");
     if (kv_len > ((int64_t)1 << 40)) return fail(LT_ERR_SHAPE, "kv_len too large");
     if (!(scale == scale) || isinf(scale)) return fail(LT_ERR_VALUE, "scale is not finite");
     if (q == nullptr || out == nullptr) return fail(LT_ERR_NULL, "q/out is NULL");

@@ -127,7 +127,6 @@ def test_decode_errors(L):
                  a["o"], a["lse"], a["ws"], a["wsb"], None)
     assert call(wsb=need - 1) == _lib.LT_ERR_WORKSPACE
     assert call(ws=None) == _lib.LT_ERR_NULL
-    assert call(Hq=34, Hkv=2) == _lib.LT_ERR_SHAPE        # G = 17 > 16
     assert call(Hq=41) == _lib.LT_ERR_SHAPE
     assert call(L=0) == _lib.LT_ERR_SHAPE
     assert call(D=80) == _lib.LT_ERR_DTYPE

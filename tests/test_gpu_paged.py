@@ -65,6 +65,8 @@ def _cases(n=40, seed=555):
         dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
         if dtype == torch.float32 and G > 8:
             G = 8
+        if i % 10 == 9:
+            G = int(rng.choice([20, 32, 40]))  # more than 16 query heads per KV head
         P = int(rng.choice([16, 32, 64, 128, 256]))
         special = [0, 1, P - 1, P, P + 1, 2 * P + 31]
         lens = [int(rng.choice(special)) if rng.random() < 0.4 else int(rng.integers(0, 3000))

@@ -140,6 +140,11 @@ DECODE_CASES = [
     (2, 4, 4, 128, 3000, torch.bfloat16, 6),   # G = 1
     (2, 10, 2, 128, 700, torch.float32, 7),
     (1, 4, 1, 64, 65, torch.float32, 8),
+    # more than 16 query heads per KV head: chunks of 16 columns
+    (1, 40, 1, 128, 3000, torch.bfloat16, 9),    # G = 40, multi-query
+    (2, 64, 2, 64, 777, torch.bfloat16, 10),     # G = 32
+    (3, 20, 1, 128, 100, torch.bfloat16, 11),    # G = 20
+    (1, 48, 2, 128, 500, torch.float32, 12),     # G = 24, fp32
 ]
 
 

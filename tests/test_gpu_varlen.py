@@ -103,6 +103,7 @@ DECODE_CASES = [
     (8, 8, 64, 700, torch.bfloat16, [700, 63, 65, 0], 43),            # G=1, D=64
     (8, 2, 64, 900, torch.float32, [900, 1, 0, 450], 44),
     (4, 1, 128, 300, torch.float32, [300, 129, 2], 45),
+    (40, 1, 128, 2000, torch.bfloat16, [2000, 0, 731, 1], 47),        # G=40: three chunks of query heads
 ]
 
 
