@@ -565,8 +565,9 @@ class Bench:
             "wall_s": round(res.wall_s, 4),
             "tflops_whole_pass": round(L64 * fl_layer / res.wall_s / 1e12, 2),
             "frac_mfma_peak_whole_pass": round(L64 * fl_layer / res.wall_s / PEAK_BF16, 4),
-            "what_is_timed": "every layer's prefill+LSE+lazy ratio, its ratios to the host (a sync per layer), "
-                             "the library's queue push and the compaction of each evicted layer",
+            "what_is_timed": "every layer's prefill+LSE+lazy ratio, its ratios to the host (a sync per layer, "
+                             "waited for once the next layer's prefill is queued), the library's queue push and "
+                             "the compaction of each evicted layer",
             "prefill_ms_mean": round(sum(res.prefill_ms) / len(res.prefill_ms), 4),
             "prefill_ms_median": round(median(res.prefill_ms), 4),
             "streaming_layers": [l for l in range(L64) if res.is_streaming[l]],

@@ -67,40 +67,22 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
     head_ratio, scores, evicted, retained, transient, times = [], [], [], [], [], []
     is_stream = [0] * layers
     full_b = stream_b = 0
-    out = lse = rows = ratio = None
-    t_start = time.perf_counter()
-    for l in range(layers):
-        q, k, v = layer_inputs(l)
-        B, Hq, N, D = q.shape
-        Hkv = k.shape[1]
-        if out is None or out.shape != q.shape or out.dtype != q.dtype:
-            out = torch.empty_like(q)
-            lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
-            rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
-            ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
-        if l == 0:
-            dt = LT_BF16 if q.dtype == torch.bfloat16 else LT_F32
-            full_b, stream_b = api.lt_kv_bytes(B, Hkv, N, D, dt, S, R)
-            queue.set_kv_bytes(full_b, stream_b, emit)
-        if timing:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-        if emit:
-            n_slots = min(N, S + R)
-            ks = torch.empty(B, Hkv, n_slots, D, device=q.device, dtype=q.dtype)
-            vs = torch.empty_like(ks)
-            api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, ks, vs)
-            slices[l] = (ks, vs)
-        else:
-            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
-        if timing:
-            e1.record()
-        r = ratio.reshape(-1).cpu().numpy()   # the per-layer device -> host sync
-        if timing:
-            times.append(e0.elapsed_time(e1))
-        kv[l] = (k, v)
-        del q
+    out = lse = rows = None
+    # Layer l's ratios go to the host through one of two pinned buffers,
+    # copied on the stream right after its prefill; the host waits for them
+    # (the per-layer device -> host sync) only after layer l + 1's prefill is
+    # queued, which does not depend on the queue's decision, so the push and
+    # the compaction of an evicted layer overlap that prefill.
+    ratio_dev: List[Optional[torch.Tensor]] = [None, None]
+    ratio_host: List[Optional[torch.Tensor]] = [None, None]
+    ready: List[Optional[torch.cuda.Event]] = [None, None]
+    pending = []   # (layer, slot, timing events) whose ratios are not read yet
+
+    def finish(l: int, slot: int, ev_pair) -> None:
+        ready[slot].synchronize()
+        r = ratio_host[slot].numpy().copy()
+        if ev_pair is not None:
+            times.append(ev_pair[0].elapsed_time(ev_pair[1]))
         ev, score = queue.push_ratios(l, r)
         held_after, held_before = queue.kv_bytes()
         transient.append(held_before)
@@ -116,6 +98,49 @@ def run(layer_inputs: Callable[[int], Tuple[torch.Tensor, torch.Tensor, torch.Te
         head_ratio.append([float(x) for x in r])
         scores.append(score)
         evicted.append(ev)
+
+    t_start = time.perf_counter()
+    for l in range(layers):
+        q, k, v = layer_inputs(l)
+        B, Hq, N, D = q.shape
+        Hkv = k.shape[1]
+        if out is None or out.shape != q.shape or out.dtype != q.dtype:
+            out = torch.empty_like(q)
+            lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
+            rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
+            for i in range(2):
+                ratio_dev[i] = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+                ratio_host[i] = torch.empty(B * Hq, dtype=torch.float32, pin_memory=True)
+                ready[i] = torch.cuda.Event()
+        if l == 0:
+            dt = LT_BF16 if q.dtype == torch.bfloat16 else LT_F32
+            full_b, stream_b = api.lt_kv_bytes(B, Hkv, N, D, dt, S, R)
+            queue.set_kv_bytes(full_b, stream_b, emit)
+        slot = l % 2
+        ratio = ratio_dev[slot]
+        ev_pair = None
+        if timing:
+            ev_pair = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            ev_pair[0].record()
+        if emit:
+            n_slots = min(N, S + R)
+            ks = torch.empty(B, Hkv, n_slots, D, device=q.device, dtype=q.dtype)
+            vs = torch.empty_like(ks)
+            api.lt_prefill_attn_lse_lazy_emit(q, k, v, out, lse, S, R, W, rows, ratio, ks, vs)
+            slices[l] = (ks, vs)
+        else:
+            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
+        if timing:
+            ev_pair[1].record()
+        ratio_host[slot].copy_(ratio.reshape(-1), non_blocking=True)
+        ready[slot].record()
+        kv[l] = (k, v)
+        del q
+        if pending:
+            finish(*pending.pop())
+        pending.append((l, slot, ev_pair))
+    while pending:
+        finish(*pending.pop())
     torch.cuda.synchronize()
     queue.close()
     return DriverResult(layers, capacity, head_ratio, scores, evicted, is_stream, retained, transient,
@@ -145,12 +170,10 @@ def offline(prompt_inputs: Callable[[int, int], Tuple[torch.Tensor, torch.Tensor
     with the lowest mean score full.  ``prompt_inputs(p, l)`` returns (q, k,
     v) of layer l on prompt p.  For comparison each prompt's test-time queue
     decision on its own ratios is reported too."""
-    ratios: List[List[List[float]]] = []
     times: List[float] = []
-    out = lse = rows = ratio = None
+    out = lse = rows = ratio_all = None
     t_start = time.perf_counter()
     for p in range(prompts):
-        per_layer = []
         for l in range(layers):
             q, k, v = prompt_inputs(p, l)
             B, Hq, N, D = q.shape
@@ -158,20 +181,22 @@ def offline(prompt_inputs: Callable[[int, int], Tuple[torch.Tensor, torch.Tensor
                 out = torch.empty_like(q)
                 lse = torch.empty(B, Hq, N, device=q.device, dtype=torch.float32)
                 rows = torch.empty(B, Hq, W, device=q.device, dtype=torch.float32)
-                ratio = torch.empty(B, Hq, device=q.device, dtype=torch.float32)
+            if ratio_all is None:
+                # every layer's ratios stay on the device until the last prefill:
+                # no decision depends on them before the selection
+                ratio_all = torch.empty(prompts, layers, B, Hq, device=q.device, dtype=torch.float32)
             if timing:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record()
-            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio)
+            api.lt_prefill_attn_lse_lazy(q, k, v, out, lse, S, R, W, rows, ratio_all[p, l])
             if timing:
                 e1.record()
-            per_layer.append(ratio.reshape(-1).cpu().numpy())
-            if timing:
-                times.append(e0.elapsed_time(e1))
+                times.append((e0, e1))
             del q, k, v
-        ratios.append(per_layer)
-    hr = np.stack([np.stack(pl) for pl in ratios])          # [P, L, n] fp32
+    hr = ratio_all.reshape(prompts, layers, -1).cpu().numpy()   # [P, L, n] fp32
+    times = [a.elapsed_time(b) for a, b in times]
+    ratios = [[hr[p, l] for l in range(layers)] for p in range(prompts)]
     layer_score, st = api.lt_select_offline(hr, capacity)
     prompt_score, test_time = [], []
     for p in range(prompts):
