@@ -511,3 +511,15 @@ def test_lt_log_prints_calls_and_their_status():
     env["LT_LOG"] = "0"
     r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "[lt] " not in r.stderr
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; --gpus N > 1 exits with status 2 and says so
+    before touching any GPU (so this runs on the CPU)."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2, (r.returncode, r.stdout[-500:], r.stderr[-500:])
+    assert "one GPU" in (r.stdout + r.stderr)
+
