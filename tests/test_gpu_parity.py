@@ -41,6 +41,7 @@ PREFILL_CASES = [
     (1, 2500, 4, 2, 64, torch.bfloat16, 4, 100, 2100, 24),  # W > 1024: the ratio's rows in several LDS rounds
     (1, 1100, 10, 2, 128, torch.bfloat16, 100, 300, 300, 25),  # sinks over two tiles, observed rows reach them
     (1, 900, 8, 1, 64, torch.bfloat16, 200, 64, 500, 26),      # sinks over two 128-key tiles
+    (1, 2300, 10, 2, 128, torch.bfloat16, 1200, 2000, 300, 27),  # long sinks and window: S + R > N
 ]
 
 
@@ -115,6 +116,9 @@ STREAM_CASES = [
     (1, 900, 10, 2, 128, torch.bfloat16, 100, 300, 13),
     (1, 1500, 8, 1, 64, torch.bfloat16, 130, 200, 14),
     (2, 700, 6, 3, 128, torch.float32, 150, 90, 15),
+    # many sink tiles before the band, and sinks past the sequence's end
+    (1, 2500, 8, 2, 128, torch.bfloat16, 1500, 37, 16),
+    (1, 900, 5, 1, 64, torch.bfloat16, 905, 3, 17),
 ]
 
 
