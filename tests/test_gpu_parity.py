@@ -149,6 +149,7 @@ DECODE_CASES = [
     (2, 64, 2, 64, 777, torch.bfloat16, 10),     # G = 32
     (3, 20, 1, 128, 100, torch.bfloat16, 11),    # G = 20
     (1, 48, 2, 128, 500, torch.float32, 12),     # G = 24, fp32
+    (64, 16, 2, 128, 300, torch.bfloat16, 13),   # large batch: one split per (sequence, KV head)
 ]
 
 

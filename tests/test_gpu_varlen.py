@@ -104,6 +104,7 @@ DECODE_CASES = [
     (8, 2, 64, 900, torch.float32, [900, 1, 0, 450], 44),
     (4, 1, 128, 300, torch.float32, [300, 129, 2], 45),
     (40, 1, 128, 2000, torch.bfloat16, [2000, 0, 731, 1], 47),        # G=40: three chunks of query heads
+    (10, 2, 64, 1200, torch.bfloat16, [(37 * i) % 1201 for i in range(33)], 48),  # B=33
 ]
 
 
