@@ -672,7 +672,6 @@ template <int D, int RB, int BT, int NW, int MODES>
 hipError_t launch_cfg(AttnArgs a, int mode, hipStream_t st) {
     const int64_t rows = (int64_t)a.N * a.G;
     const int brows = NW * 16 * RB;
-    a.n_chunks = 1;
     a.n_qtiles = (int)((rows + brows - 1) / brows);
     dim3 grid((unsigned)(a.n_qtiles * a.B * a.Hkv));
     dim3 block(64 * NW);

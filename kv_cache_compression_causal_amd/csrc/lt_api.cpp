@@ -99,7 +99,7 @@ lt::AttnArgs make_args(const lt_shape *s, const lt_view &q, const lt_view &k, co
     a.v_sb = v.sb; a.v_sh = v.sh; a.v_sn = v.sn;
     a.o_sb = out.sb; a.o_sh = out.sh; a.o_sn = out.sn;
     a.B = s->B; a.N = s->N; a.Hq = s->Hq; a.Hkv = s->Hkv; a.G = s->Hq / s->Hkv;
-    a.n_chunks = 1; a.n_qtiles = 1;
+    a.n_qtiles = 1;
     a.scale = s->scale > 0.f ? s->scale : 1.f / sqrtf((float)s->D);
     a.c = a.scale * 1.4426950408889634f;
     a.S = S; a.R = R; a.W = W;

@@ -43,7 +43,6 @@ struct AttnArgs {
     int64_t v_sb, v_sh, v_sn;
     int64_t o_sb, o_sh, o_sn;
     int B, N, Hq, Hkv, G;
-    int n_chunks;   // query heads of a group are split into n_chunks chunks
     int n_qtiles;   // query tiles per (b, kv head, chunk)
     float scale;    // softmax scale
     float c;        // scale * log2(e)
